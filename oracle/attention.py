@@ -1,0 +1,133 @@
+"""Plain fp64 CPU oracle for exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module; the GPU path never calls it and shares no code
+with it.  It materialises the full score matrix S and probability matrix P, in
+float64, with no tiling and no online recurrence: it is the definition the fused
+kernels must reproduce up to rounding order.
+
+Sources (pages, with the part of each page followed):
+  [FAN] page "FlashAttention" (vagrantpi.github.io PKM note), part "標準 attention
+        在幹嘛（IO 的角度）": S = QK^T/sqrt(d), P = softmax(S), O = PV; and "三招"
+        item 3 (Recomputation): the forward keeps O and the per-row softmax
+        statistics, the backward rebuilds P from them.
+  [XH]  page "知识点13 | FlashAttention深度攻略" (blog.xiaohack.org):
+        section 2 (standard attention formula softmax(QK^T/sqrt(d_k))V),
+        section 4 (numerically safe softmax: subtract the row maximum),
+        the function standard_attention under "标准注意力对比" (scale, then a
+        causal mask that sets entries above the diagonal to -inf, then a row
+        softmax, then the product with V), and section 6 (backward).
+  [GWL] page "Flash Attention 到底做了什么？" (guanweilu.cn), section
+        "它不是一个近似算法": the fused method equals the plain computation except
+        for floating-point rounding order, so the plain computation is the oracle.
+
+Readings taken where the pages are silent or garbled:
+  * The saved statistics are the natural-log logsumexp LSE_i = m_i + ln(l_i) per
+    query row (the pages save the pair (m, l); LSE carries the same information).
+  * The causal mask hides key j from query i when j > i, by absolute index
+    (standard_attention's triu(diagonal=1) over the full matrix).
+  * The backward formula printed in [XH] section 6 is garbled; the oracle uses
+    the chain rule of softmax: dV = P^T dO, dP = dO V^T, D_i = sum_j P_ij dP_ij,
+    dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+  * A row whose keys are all masked has no softmax; it is defined as O = 0 and
+    LSE = -inf (this cannot happen for square causal attention).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "scores", "softmax_rows", "forward", "forward_rows", "backward",
+    "forward_bnhd", "backward_bnhd",
+]
+
+
+def _as64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def scores(q, k, scale, causal, rows=None):
+    """S = scale * q k^T with the causal mask applied ([XH] standard_attention).
+
+    q: [nq, d] query rows; k: [nk, d]; rows: absolute query index of each q row
+    (default 0..nq-1).  Masked entries are -inf.
+    """
+    q, k = _as64(q), _as64(k)
+    s = float(scale) * (q @ k.T)
+    if causal:
+        qi = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+        hidden = np.arange(k.shape[0])[None, :] > qi[:, None]
+        s = np.where(hidden, -np.inf, s)
+    return s
+
+
+def softmax_rows(s):
+    """Row softmax with the row maximum subtracted first ([XH] section 4).
+
+    Returns (P, m, l, lse): P = exp(S - m) / l, m the row max, l the row sum of
+    exp(S - m), lse = m + ln l.  Fully masked rows give P = 0, lse = -inf.
+    """
+    m = s.max(axis=1)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])          # exp(-inf) = 0 for masked entries
+    l = e.sum(axis=1)
+    l_safe = np.where(empty, 1.0, l)
+    p = e / l_safe[:, None]
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))
+    return p, m, l, lse
+
+
+def forward(q, k, v, scale, causal):
+    """One head: O = softmax(scale q k^T [+mask]) v and the per-row LSE."""
+    p, _, _, lse = softmax_rows(scores(q, k, scale, causal))
+    return p @ _as64(v), lse
+
+
+def forward_rows(q_rows, rows, k, v, scale, causal):
+    """O and LSE for a subset of query rows (absolute indices `rows`) of one head."""
+    p, _, _, lse = softmax_rows(scores(q_rows, k, scale, causal, rows=rows))
+    return p @ _as64(v), lse
+
+
+def backward(q, k, v, do, scale, causal):
+    """One head: (dQ, dK, dV) of the loss sum(O * dO), by the chain rule.
+
+    Also returns D_i = sum_j P_ij dP_ij, which equals rowsum(dO * O).
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    p, _, _, _ = softmax_rows(scores(q, k, scale, causal))
+    dv = p.T @ do
+    dp = do @ v.T
+    dvec = (p * dp).sum(axis=1)
+    ds = p * (dp - dvec[:, None])
+    dq = float(scale) * (ds @ k)
+    dk = float(scale) * (ds.T @ q)
+    return dq, dk, dv, dvec
+
+
+# ----------------------------------------------------------------- [B, N, H, d] helpers
+
+def forward_bnhd(q, k, v, scale, causal, heads=None):
+    """Apply :func:`forward` to each (b, h) of [B, N, H, d] float64 tensors.
+
+    heads: iterable of (b, h) pairs (default: all).  Returns dicts keyed by (b, h).
+    """
+    B, _, H, _ = q.shape
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    o, lse = {}, {}
+    for b, h in heads:
+        o[(b, h)], lse[(b, h)] = forward(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal)
+    return o, lse
+
+
+def backward_bnhd(q, k, v, do, scale, causal, heads=None):
+    """Apply :func:`backward` to each (b, h); returns dicts of dq, dk, dv, D."""
+    B, _, H, _ = q.shape
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    res = {"dq": {}, "dk": {}, "dv": {}, "D": {}}
+    for b, h in heads:
+        dq, dk, dv, dvec = backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal)
+        res["dq"][(b, h)], res["dk"][(b, h)], res["dv"][(b, h)], res["D"][(b, h)] = dq, dk, dv, dvec
+    return res
