@@ -1,0 +1,39 @@
+"""Fused, IO-aware exact attention for MI355X (gfx950), behind the C ABI of libfa.so.
+
+    o, lse = forward(q, k, v, scale=None, causal=False)
+    dq, dk, dv = backward(q, k, v, o, do, lse, scale=None, causal=False)
+
+Tensors are contiguous [B, N, H, d] bf16 (or fp32) CUDA tensors with d in
+{64, 128}; lse is fp32 [B, H, N].  scale defaults to d**-0.5, as in the PyTorch
+module on the page "知识点13 | FlashAttention深度攻略" (blog.xiaohack.org).
+PyTorch only supplies device memory and the current stream: every step runs in
+the HIP kernels of libfa.so.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_workspace_bytes,  # noqa: F401
+                   fa_forward, fa_status_string, load)
+
+
+def _scale(q, scale):
+    return float(q.shape[-1]) ** -0.5 if scale is None else float(scale)
+
+
+def forward(q, k, v, scale=None, causal=False, stream=None):
+    """O and LSE of exact attention; allocates the outputs on q's device."""
+    B, N, H, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_forward(q, k, v, o, lse, _scale(q, scale), causal, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, do, lse, scale=None, causal=False, stream=None):
+    """dQ, dK, dV of sum(O * dO); allocates the outputs and the workspace."""
+    B, N, H, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device=q.device)
+    fa_backward(q, k, v, o, do, lse, dq, dk, dv, ws, _scale(q, scale), causal, stream)
+    return dq, dk, dv

@@ -1,0 +1,111 @@
+"""ctypes binding of libfa.so (include/fa.h).
+
+Argument marshalling only: each function here turns torch tensors into device
+pointers and sizes and calls the C entry point of the same name on the current
+torch stream.  Nothing is computed in Python and there is no fallback: if the
+library is missing or a call fails, an exception says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_39_amd.build` "
+            "(there is no non-HIP implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    fwd_args = [P, P, P, P, P, I, I, I, I, F, I, P]
+    bwd_args = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P]
+    for name, args in (("fa_forward", fwd_args), ("fa_forward_f32", fwd_args),
+                       ("fa_backward", bwd_args), ("fa_backward_f32", bwd_args)):
+        fn = getattr(lib, name)
+        fn.argtypes, fn.restype = args, I
+    lib.fa_backward_workspace_bytes.argtypes = [I, I, I, I]
+    lib.fa_backward_workspace_bytes.restype = S
+    lib.fa_status_string.argtypes = [I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_backward_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load().fa_backward_workspace_bytes(B, H, N, d))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError(f"expected a [B, N, H, d] tensor, got shape {tuple(q.shape)}")
+    return tuple(int(x) for x in q.shape)
+
+
+def _check(ts, dtype):
+    for t in ts:
+        if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+            raise ValueError(f"expected contiguous {dtype} CUDA tensors, got {t.dtype} on {t.device}")
+
+
+def _call(name, status):
+    if status != FA_OK:
+        raise FaError(status, name)
+
+
+def fa_forward(q, k, v, o, lse, scale: float, causal: bool, stream=None):
+    """fa_forward / fa_forward_f32 on [B, N, H, d] tensors (bf16 or fp32)."""
+    B, N, H, d = _shape(q)
+    name = "fa_forward" if q.dtype == torch.bfloat16 else "fa_forward_f32"
+    _check((q, k, v, o), q.dtype)
+    _check((lse,), torch.float32)
+    fn = getattr(load(), name)
+    _call(name, fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                   int(bool(causal)), _stream(stream)))
+
+
+def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float, causal: bool, stream=None):
+    """fa_backward / fa_backward_f32 on [B, N, H, d] tensors (bf16 or fp32)."""
+    B, N, H, d = _shape(q)
+    name = "fa_backward" if q.dtype == torch.bfloat16 else "fa_backward_f32"
+    _check((q, k, v, o, do, dq, dk, dv), q.dtype)
+    _check((lse, workspace), torch.float32)
+    if workspace.numel() * 4 < fa_backward_workspace_bytes(B, H, N, d):
+        raise ValueError("workspace smaller than fa_backward_workspace_bytes()")
+    fn = getattr(load(), name)
+    _call(name, fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                   _ptr(dv), _ptr(workspace), B, H, N, d, float(scale), int(bool(causal)),
+                   _stream(stream)))

@@ -1,0 +1,106 @@
+// fa_api.cpp - the C ABI of libfa.so: argument validation and dispatch.
+//
+// Every check runs on the host before any HIP call, so a rejected call has no
+// side effect on the device and the checks can be exercised without a GPU.
+// There is no fallback path: an unsupported head size is an error, never a
+// silent switch to a slower kernel.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <climits>
+
+#include "../../include/fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape, scale and mask checks shared by every entry point.
+fa_status check_common(int B, int H, int N, int d, float scale, int causal) {
+  if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (scale < 0.f) return FA_ERR_UNSUPPORTED;
+  if (N > (1 << 20)) return FA_ERR_UNSUPPORTED;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > (1 << 20)) return FA_ERR_UNSUPPORTED;
+  if (bh * N * d >= ((int64_t)1 << 40)) return FA_ERR_UNSUPPORTED;
+  // The largest grid any kernel uses: one workgroup per 64 rows of each head.
+  if (bh * ((N + 63) / 64) > INT_MAX) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+fa_status check_tensors(std::initializer_list<const void*> tensors, std::initializer_list<const void*> stats) {
+  for (const void* p : tensors)
+    if (p == nullptr || !aligned(p, 16)) return FA_ERR_INVALID_ARG;
+  for (const void* p : stats)
+    if (p == nullptr || !aligned(p, 4)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+fa_status to_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int B, int H, int N, int d, float scale, int causal, void* stream) {
+  fa_status st = check_common(B, H, N, d, scale, causal);
+  if (st == FA_OK) st = check_tensors({Q, K, V, O}, {LSE});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal};
+  return to_status(fa::launch_fwd_bf16(Q, K, V, O, LSE, s, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
+                         int B, int H, int N, int d, float scale, int causal, void* stream) {
+  fa_status st = check_common(B, H, N, d, scale, causal);
+  if (st == FA_OK) st = check_tensors({Q, K, V, O}, {LSE});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal};
+  return to_status(fa::launch_fwd_f32(Q, K, V, O, LSE, s, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
+                      int B, int H, int N, int d, float scale, int causal, void* stream) {
+  fa_status st = check_common(B, H, N, d, scale, causal);
+  if (st == FA_OK) st = check_tensors({Q, K, V, O, dO, dQ, dK, dV}, {LSE, workspace});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal};
+  return to_status(fa::launch_bwd_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, s,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_backward_f32(const float* Q, const float* K, const float* V, const float* O,
+                          const float* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                          float* workspace, int B, int H, int N, int d, float scale, int causal,
+                          void* stream) {
+  fa_status st = check_common(B, H, N, d, scale, causal);
+  if (st == FA_OK) st = check_tensors({Q, K, V, O, dO, dQ, dK, dV}, {LSE, workspace});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal};
+  return to_status(fa::launch_bwd_f32(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, s,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
+  if (check_common(B, H, N, d, 1.f, 0) != FA_OK) return 0;
+  return (size_t)B * H * N * sizeof(float);
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument (null or misaligned pointer, bad size, scale or mask flag)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration (head size other than 64/128, negative scale, or size limits)";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: a HIP launch failed";
+    default: return "unknown fa_status";
+  }
+}
+
+}  // extern "C"

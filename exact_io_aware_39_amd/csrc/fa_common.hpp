@@ -1,0 +1,128 @@
+// fa_common.hpp - shared device helpers for the gfx950 attention kernels.
+//
+// MFMA fragment conventions (v_mfma_f32_32x32x16_bf16, wave64), checked on the
+// device with a probe of known matrices:
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. 8*(l/32)+7
+//   B (16 x 32): lane l holds column l%32, the same k range as A
+//   C (32 x 32): lane l, register r holds column l%32,
+//                row 8*(r/4) + 4*(l/32) + r%4
+// Only the pairing of A's and B's k slots matters for a contraction, so any
+// permutation of k applied to both operands is free; the kernels use that to
+// feed a C fragment straight back in as a B operand.
+//
+// LDS tiles hold rows of D bf16 values (D*2 bytes) whose 16-byte chunks are
+// permuted per row (chunk ^ swz(row)) so that both the row reads of the score
+// product and the transposing reads of the value product hit distinct banks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of x held by lane (l + 32) % 64, i.e. the other half of the wave.
+__device__ __forceinline__ float other_half(float x) {
+  const int lane = __lane_id();
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Round 8 floats to bf16 (nearest even) and pack them as one MFMA operand.
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3,
+                                              float a4, float a5, float a6, float a7) {
+  bf16x2 p0 = __builtin_convertvector((f32x2){a0, a1}, bf16x2);
+  bf16x2 p1 = __builtin_convertvector((f32x2){a2, a3}, bf16x2);
+  bf16x2 p2 = __builtin_convertvector((f32x2){a4, a5}, bf16x2);
+  bf16x2 p3 = __builtin_convertvector((f32x2){a6, a7}, bf16x2);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+__device__ __forceinline__ bf16x4 pack_bf16x4(float a0, float a1, float a2, float a3) {
+  bf16x2 p0 = __builtin_convertvector((f32x2){a0, a1}, bf16x2);
+  bf16x2 p1 = __builtin_convertvector((f32x2){a2, a3}, bf16x2);
+  bf16x4 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  return r;
+}
+
+// Per-row chunk permutation for a tile with rows of D bf16 values.
+//  D = 128 (16 chunks, 256 B a row): the 4 low row bits, rotated by 2, so 16
+//    consecutive rows read at one chunk land in 16 different chunk slots, and 4
+//    consecutive rows read over 4 aligned chunks cover 16 different slots.
+//  D = 64 (8 chunks, 128 B a row, two rows per 256 B bank window): rows of one
+//    parity get 8 different slots for rows 0..15, and rows 2 apart differ in
+//    chunk bit 2.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+}
+
+// Byte offset of 16-byte chunk `chunk` of row `row` inside an LDS tile.
+template <int D>
+__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
+  return (uint32_t)(row * (D * 2) + ((chunk ^ swz<D>(row)) << 4));
+}
+
+// Byte offset of bf16 element (row, col) inside an LDS tile.
+template <int D>
+__device__ __forceinline__ uint32_t elem_off(int row, int col) {
+  return tile_off<D>(row, col >> 3) + (uint32_t)((col & 7) << 1);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* base, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+
+// Transposing LDS read of 4 bf16 values (ds_read_b64_tr_b16).  Within each
+// group of 16 lanes, lane i receives element i%4 of the 8-byte rows addressed
+// by lanes i/4, 4+i/4, 8+i/4, 12+i/4 of that group, in that order.
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* base, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + off));
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
+// XCD runs one contiguous range of logical tiles (neighbouring tiles share the
+// same K/V rows and so the same L2).
+__device__ __forceinline__ int xcd_remap(int id, int count) {
+  const int x = id & 7, slot = id >> 3;
+  const int q = count >> 3, r = count & 7;
+  return x * q + (x < r ? x : r) + slot;
+}
+
+}  // namespace fa

@@ -1,0 +1,28 @@
+// fa_launch.hpp - host-side launchers shared by the C ABI and the kernel files.
+// Every launcher assumes arguments already validated by fa_api.cpp and returns
+// the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct AttnShape {
+  int B, H, N, d;
+  float scale;
+  int causal;
+};
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const AttnShape& s, hipStream_t stream);
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          const AttnShape& s, hipStream_t stream);
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           float* dvec, const AttnShape& s, hipStream_t stream);
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                          const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                          float* dvec, const AttnShape& s, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,114 @@
+/*
+ * fa.h - C ABI of libfa.so: fused, IO-aware exact attention for MI355X (gfx950).
+ *
+ * Computes O = softmax(scale * Q K^T [+ causal mask]) V for every (batch, head)
+ * without writing the N x N score or probability matrices to memory, and the
+ * gradients of a loss with respect to Q, K and V by recomputing the
+ * probabilities from a per-row logsumexp saved by the forward.
+ *
+ * Sources (web pages, with the part each entry point follows):
+ *   page "FlashAttention" (vagrantpi.github.io PKM note): the IO view of
+ *     standard attention (S = QK^T/sqrt(d), P = softmax(S), O = PV) and its
+ *     three techniques: tiling, the online-softmax recurrence (running max,
+ *     running sum, rescaled unnormalised output, one final divide) and
+ *     recomputation in the backward from saved row statistics.
+ *   page "知识点13 | FlashAttention深度攻略" (blog.xiaohack.org): section 2
+ *     (softmax(QK^T/sqrt(d_k))V), section 3 (blocks of B_r query rows and B_c
+ *     key rows), section 6 (backward with recomputation), section 7 (one fused
+ *     kernel), and the PyTorch module under "代码手撕环节" whose forward takes
+ *     (batch, seq_len, num_heads, head_dim) tensors, uses scale = head_dim^-0.5
+ *     and an optional causal mask that hides key j from query i when j > i.
+ *   page "Flash Attention 到底做了什么？" (guanweilu.cn): section on the backward
+ *     (keep per-row statistics, recompute S instead of storing it).
+ *
+ * Conventions shared by every entry point:
+ *   Layout    Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, N, H, d]
+ *             tensors (element (b, n, h, c) at ((b*N + n)*H + h)*d + c).
+ *             LSE and the backward workspace are dense float32 [B, H, N].
+ *   Masking   causal = 1 hides key j from query i when j > i (absolute index,
+ *             square attention: queries and keys share the length N).
+ *   Scale     the float32 factor applied to Q K^T; it must be finite and >= 0
+ *             (the pages use head_dim^-0.5).
+ *   LSE       natural-log logsumexp of each row of scale * Q K^T (masked
+ *             entries excluded): O = exp(scale q_i K^T - LSE_i) V.
+ *   Ownership the caller allocates and owns every buffer (device memory of
+ *             the current device).  The library allocates, frees and
+ *             synchronises nothing.
+ *   Streams   work is enqueued asynchronously on `stream` (a hipStream_t;
+ *             NULL means the null stream).  Device faults surface at the
+ *             caller's next synchronisation, as for any HIP launch.
+ *   Errors    arguments are validated on the host before any HIP call:
+ *               FA_ERR_INVALID_ARG  null pointer, a tensor pointer not 16-byte
+ *                                   aligned, an LSE/workspace pointer not
+ *                                   4-byte aligned, B, H or N <= 0, a
+ *                                   non-finite scale, causal not 0 or 1;
+ *               FA_ERR_UNSUPPORTED  d not 64 or 128, scale < 0, or sizes
+ *                                   beyond the limits below; there is no
+ *                                   fallback path;
+ *               FA_ERR_LAUNCH       a HIP call or kernel launch failed.
+ *             On error nothing has been enqueued.
+ *   Limits    N <= 2^20, B*H <= 2^20, B*N*H*d < 2^40 elements.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_LAUNCH = 3
+} fa_status;
+
+/*
+ * Forward, bfloat16 tensors (fp32 accumulation).  Q, K, V are read; O
+ * ([B, N, H, d] bf16, rounded to nearest even) and LSE ([B, H, N] fp32) are
+ * written.  Tiling and online softmax: page "FlashAttention", techniques 1
+ * and 2; the saved statistics of technique 3 are returned as LSE.
+ */
+fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * Forward, float32 tensors: same contract as fa_forward with every tensor
+ * float32 (fp32 products and accumulation throughout).
+ */
+fa_status fa_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
+                         int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * Backward, bfloat16 tensors.  Given the forward's inputs, its O and LSE
+ * (unchanged), and dO = dLoss/dO, writes dQ, dK, dV (bf16, [B, N, H, d]).
+ * P is rebuilt from LSE (page "FlashAttention", technique 3; page "知识点13 |
+ * FlashAttention深度攻略", section 6) and the gradients follow the chain rule
+ * of softmax: dV = P^T dO, dP = dO V^T, D_i = rowsum(dO * O)_i,
+ * dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ * `workspace` is caller-owned device memory of fa_backward_workspace_bytes()
+ * bytes; on return it holds D ([B, H, N] fp32).
+ */
+fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
+                      int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Backward, float32 tensors: same contract as fa_backward, every tensor fp32. */
+fa_status fa_backward_f32(const float* Q, const float* K, const float* V, const float* O,
+                          const float* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                          float* workspace, int B, int H, int N, int d, float scale, int causal,
+                          void* stream);
+
+/* Bytes of workspace fa_backward / fa_backward_f32 need (0 for invalid sizes). */
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

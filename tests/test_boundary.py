@@ -1,0 +1,126 @@
+"""The C ABI on the host: exported symbols and argument validation (no GPU).
+
+Every call below is rejected by the library's host-side checks, which run
+before any HIP call, so nothing is launched.  Pointer values are fake but
+never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+LIB = os.path.join(ROOT, "exact_io_aware_39_amd", "libfa.so")
+
+OK, INVALID, UNSUPPORTED, LAUNCH = 0, 1, 2, 3
+P = 0x10000          # a 16-byte aligned fake device address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libfa.so not built: run python -m exact_io_aware_39_amd.build")
+    lib = ctypes.CDLL(LIB)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    for name in ("fa_forward", "fa_forward_f32"):
+        getattr(lib, name).argtypes = [vp] * 5 + [i] * 4 + [f, i, vp]
+        getattr(lib, name).restype = i
+    for name in ("fa_backward", "fa_backward_f32"):
+        getattr(lib, name).argtypes = [vp] * 10 + [i] * 4 + [f, i, vp]
+        getattr(lib, name).restype = i
+    lib.fa_backward_workspace_bytes.argtypes = [i] * 4
+    lib.fa_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted([
+        "fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_f32",
+        "fa_backward_workspace_bytes", "fa_status_string"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _fwd(lib, name="fa_forward", ptrs=(P, P, P, P, P), B=1, H=1, N=128, d=64, scale=0.125, causal=0):
+    return getattr(lib, name)(*ptrs, B, H, N, d, scale, causal, None)
+
+
+def _bwd(lib, name="fa_backward", ptrs=(P,) * 10, B=1, H=1, N=128, d=64, scale=0.125, causal=0):
+    return getattr(lib, name)(*ptrs, B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("name", ["fa_forward", "fa_forward_f32"])
+def test_forward_rejects_bad_arguments(lib, name):
+    for d in (0, 32, 96, 256):
+        assert _fwd(lib, name, d=d) == UNSUPPORTED
+    for B, H, N in ((0, 1, 8), (1, 0, 8), (1, 1, 0), (-1, 1, 8)):
+        assert _fwd(lib, name, B=B, H=H, N=N) == INVALID
+    assert _fwd(lib, name, N=(1 << 20) + 1) == UNSUPPORTED
+    assert _fwd(lib, name, B=1 << 11, H=1 << 10) == UNSUPPORTED
+    for s in (float("nan"), float("inf"), float("-inf")):
+        assert _fwd(lib, name, scale=s) == INVALID
+    assert _fwd(lib, name, scale=-0.5) == UNSUPPORTED
+    assert _fwd(lib, name, causal=2) == INVALID
+    assert _fwd(lib, name, causal=-1) == INVALID
+    for i in range(5):
+        ptrs = [P] * 5
+        ptrs[i] = None
+        assert _fwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+    for i in range(4):                       # tensors need 16-byte alignment
+        ptrs = [P] * 5
+        ptrs[i] = P + 8
+        assert _fwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+    assert _fwd(lib, name, ptrs=(P, P, P, P, P + 2)) == INVALID   # LSE needs 4-byte alignment
+
+
+@pytest.mark.parametrize("name", ["fa_backward", "fa_backward_f32"])
+def test_backward_rejects_bad_arguments(lib, name):
+    assert _bwd(lib, name, d=80) == UNSUPPORTED
+    assert _bwd(lib, name, N=0) == INVALID
+    assert _bwd(lib, name, scale=float("nan")) == INVALID
+    assert _bwd(lib, name, causal=3) == INVALID
+    for i in range(10):
+        ptrs = [P] * 10
+        ptrs[i] = None
+        assert _bwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+    for i in (0, 1, 2, 3, 4, 6, 7, 8):         # Q K V O dO dQ dK dV: 16-byte alignment
+        ptrs = [P] * 10
+        ptrs[i] = P + 4
+        assert _bwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+    for i in (5, 9):                          # LSE and workspace: 4-byte alignment
+        ptrs = [P] * 10
+        ptrs[i] = P + 2
+        assert _bwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+
+
+def test_workspace_bytes(lib):
+    assert lib.fa_backward_workspace_bytes(2, 16, 8192, 64) == 2 * 16 * 8192 * 4
+    assert lib.fa_backward_workspace_bytes(1, 1, 1, 128) == 4
+    assert lib.fa_backward_workspace_bytes(0, 16, 8192, 64) == 0
+    assert lib.fa_backward_workspace_bytes(2, 16, 8192, 96) == 0
+
+
+def test_status_strings(lib):
+    for code, key in ((OK, b"FA_OK"), (INVALID, b"FA_ERR_INVALID_ARG"),
+                      (UNSUPPORTED, b"FA_ERR_UNSUPPORTED"), (LAUNCH, b"FA_ERR_LAUNCH")):
+        assert lib.fa_status_string(code).startswith(key)
+    assert b"unknown" in lib.fa_status_string(99)
+
+
+def test_python_binding_reports_status_names():
+    from exact_io_aware_39_amd import fa_status_string, FaError
+    assert fa_status_string(2).startswith("FA_ERR_UNSUPPORTED")
+    assert "FA_ERR_INVALID_ARG" in str(FaError(1, "fa_forward"))
