@@ -1,0 +1,97 @@
+"""GPU backward (fa_backward / fa_backward_f32) against the fp64 CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as ora
+import synth
+from gpu_helpers import check, inputs, require_gpu, say, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    import exact_io_aware_39_amd as fa
+    fa.load()
+
+
+def fa_mod():
+    import exact_io_aware_39_amd as fa
+    return fa
+
+
+def sum_bound(x):
+    """Allowed |sum error| for a sum of rounded gradient rows: 5 sigma of
+    independent relative errors of 2^-8 / sqrt(3) from the bf16 rounding of
+    the output and of the products' operands."""
+    return 5 * 2 * 2.0 ** -8 / np.sqrt(3) * float(np.sqrt((x ** 2).sum(axis=0)).max()) + 1e-6
+
+
+def run_and_check(shape, dtype, seed, causal, scale, heads=None, tag=""):
+    fa = fa_mod()
+    say(f"backward {tag} shape={shape} dtype={dtype} causal={causal} seed={seed}")
+    dev, f64 = inputs(shape, dtype, seed, with_do=True)
+    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], scale=scale, causal=causal)
+    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    B, N, H, d = shape
+    heads = heads or [(b, h) for b in range(B) for h in range(H)]
+    worst = {}
+    for b, h in heads:
+        q, k, v, do = (f64[n][b, :, h] for n in ("q", "k", "v", "do"))
+        dq_r, dk_r, dv_r, _ = ora.backward(q, k, v, do, scale, causal)
+        for name, got, ref in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
+            e = check(to64(got[b, :, h]), ref, dtype, f"{name} b={b} h={h} {tag}")
+            worst[name] = max(worst.get(name, (0, 0)), e)
+    say(f"  ok: worst (max, mean) abs err {worst}")
+    return dev, f64, (o, lse), (dq, dk, dv)
+
+
+def test_c5_backward_and_invariants():
+    w = synth.WORKLOADS["c5"]
+    dev, f64, _, (dq, dk, dv) = run_and_check(w.shape, w.dtype, w.seed, True, w.scale,
+                                              heads=synth.checked_heads(w), tag="c5")
+    # Invariants on every head: rows of P sum to one (sum_j dV_j = sum_i dO_i)
+    # and shift invariance of softmax (sum_j dK_j = 0).
+    dv64 = dv.double().sum(dim=1).cpu().numpy()           # [B, H, d]
+    do64 = dev["do"].double().sum(dim=1).cpu().numpy()
+    dk64 = dk.double().sum(dim=1).cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.H):
+            dvh, dkh = to64(dv[b, :, h]), to64(dk[b, :, h])
+            assert np.abs(dv64[b, h] - do64[b, h]).max() <= sum_bound(dvh), f"sum dV b={b} h={h}"
+            assert np.abs(dk64[b, h]).max() <= sum_bound(dkh), f"sum dK b={b} h={h}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 17, 100, 129, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_ragged_bf16(N, d, causal):
+    run_and_check((2, N, 2, d), "bf16", 3000 + N + d, causal, d ** -0.5, tag="ragged")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 45, 130])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_ragged_fp32(N, d, causal):
+    run_and_check((1, N, 2, d), "f32", 4000 + N + d, causal, d ** -0.5, tag="ragged-f32")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_d128_midsize(causal):
+    run_and_check((1, 2048, 4, 128), "bf16", 5005, causal, 128 ** -0.5, heads=[(0, 1), (0, 3)], tag="d128")
+
+
+def test_backward_is_deterministic():
+    fa = fa_mod()
+    shape = (1, 1000, 3, 64)
+    say("backward determinism")
+    dev, _ = inputs(shape, "bf16", 6006, with_do=True)
+    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=True)
+    r1 = fa.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True)
+    r2 = fa.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
