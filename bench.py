@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the fused exact-attention hot path on one MI355X.
+
+One step = one forward (fa_forward) and one backward (fa_backward_preprocess,
+fa_backward_dkdv, fa_backward_dq - exactly what fa_backward runs) of bf16
+causal attention on the forward+backward workload [B, N, H, d] = [2, 8192, 16,
+64], scale 1/8, inputs seeded N(0, 1) and already resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Prints one JSON line.  value = credited TFLOP/s of the whole step, with the
+forward credited 4 B H N^2 d / 2 FLOPs (causal) and the backward 2.5 times
+that.  `roofline` covers the kernel with the largest average duration,
+timed with HIP events recorded around each launch on the stream the kernels
+run on.  `cpu_baseline` times the fp64 CPU oracle on one head of the same
+workload.  `forward_only` times the forward alone on the two long causal
+workloads ([4, 4096, 16, 128] and [1, 32768, 32, 128] with Q, K doubled).
+
+    python bench.py --copy-calibration
+
+runs only a plain device copy of 256 MiB (for scaling hardware byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention TFLOP/s (bf16 fwd & fwd+bwd, causal) and % of MI355X MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_flops(B, H, N, d, causal):
+    return 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+
+
+def copy_calibration():
+    import torch
+    n = 256 * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 launches, each reads {n * 4} B and writes {n * 4} B")
+
+
+def kernel_traffic(name):
+    """HBM bytes per launch from a committed counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    src = re.search(r"source_file:\s*(\S+)", text)
+    if not (m and h and src):
+        return None
+    cur = hashlib.sha256(open(os.path.join(ROOT, src.group(1)), "rb").read()).hexdigest()
+    return float(m.group(1)) if cur == h.group(1) else None
+
+
+def time_forward_only(fa, torch, B, N, H, d, scale, qk_mult, seed, iters):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    q = (torch.randn((B, N, H, d), generator=g, device="cuda", dtype=torch.float32) * qk_mult).to(torch.bfloat16)
+    k = (torch.randn((B, N, H, d), generator=g, device="cuda", dtype=torch.float32) * qk_mult).to(torch.bfloat16)
+    v = torch.randn((B, N, H, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        fa.fa_forward(q, k, v, o, lse, scale, True)
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record(st)
+    for i in range(iters):
+        fa.fa_forward(q, k, v, o, lse, scale, True)
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+    med = ms[len(ms) // 2]
+    tf = fwd_flops(B, H, N, d, True) / (med * 1e-3) / 1e12
+    del q, k, v, o, lse
+    return {"shape_BNHd": [B, N, H, d], "causal": True, "median_ms": round(med, 4),
+            "tflops": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
+
+
+def cpu_baseline(w, host, got, min_seconds=10.0):
+    """Time the fp64 oracle (forward + backward) on whole heads of the workload,
+    head after head, until at least `min_seconds` of CPU work; also compare the
+    first head with the GPU results."""
+    import numpy as np
+    import oracle.attention as ora
+    import synth
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"), default=1)
+    except Exception:   # threadpoolctl missing: fall back to the affinity mask
+        threads = len(os.sched_getaffinity(0))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    errs, done, dt = {}, 0, 0.0
+    for b, h in heads:
+        q, k, v, do = (synth.decode(host[n][b, :, h]) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        o_ref, lse_ref = ora.forward(q, k, v, w.scale, True)
+        dq_ref, dk_ref, dv_ref, _ = ora.backward(q, k, v, do, w.scale, True)
+        dt += time.perf_counter() - t0
+        done += 1
+        if done == 1:
+            for name, ref in (("O", o_ref), ("dQ", dq_ref), ("dK", dk_ref), ("dV", dv_ref)):
+                g = got[name][b, :, h].float().cpu().numpy().astype(np.float64)
+                errs[name] = float(np.abs(g - ref).max())
+            lg = got["LSE"][b, h].cpu().numpy().astype(np.float64)
+            errs["LSE_rel"] = float(np.max(np.abs(lg - lse_ref) / np.maximum(1, np.abs(lse_ref))))
+        if dt >= min_seconds:
+            break
+    flops = fwd_flops(1, 1, w.N, w.d, True) * 3.5 * done
+    return {
+        "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, forward + backward of {done} whole head(s) of the same workload "
+                   f"(N={w.N}, d={w.d}, causal) in {dt:.1f} s; credited FLOPs as for the GPU"),
+        "seconds": round(dt, 2),
+    }, errs
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md on "
+              "sharding); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import exact_io_aware_39_amd as fa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    w = synth.WORKLOADS["c5"]
+    B, N, H, d = w.shape
+    log(f"bench: workload c5 [B,N,H,d]={list(w.shape)} bf16 causal scale={w.scale}")
+    host = synth.workload_inputs(w)
+    dev = {k: torch.from_numpy(v.view(np.int16)).cuda().view(torch.bfloat16) for k, v in host.items()}
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(st)
+        fa.fa_forward(q, k, v, o, lse, w.scale, True)
+        if evs:
+            evs[1].record(st)
+        fa.fa_backward_preprocess(o, do, ws)
+        if evs:
+            evs[2].record(st)
+        fa.fa_backward_dkdv(q, k, v, do, lse, ws, dk, dv, w.scale, True)
+        if evs:
+            evs[3].record(st)
+        fa.fa_backward_dq(q, k, v, do, lse, ws, dq, w.scale, True)
+        if evs:
+            evs[4].record(st)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+    per = {n: [events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)] for j, n in enumerate(names)}
+    avg = {n: sum(x) / len(x) for n, x in per.items()}
+    ms_step = wall * 1e3 / args.steps
+
+    F = fwd_flops(B, H, N, d, True)
+    Fb = 2.5 * F
+    value = (F + Fb) / (ms_step * 1e-3) / 1e12
+    fwd_ms = avg["fwd"]
+    bwd_ms = avg["bwd_preprocess"] + avg["bwd_dkdv"] + avg["bwd_dq"]
+    pairs = B * H * N * N / 2.0                      # visible (query, key) pairs, causal
+    alg = {   # algorithmic work of one launch of each kernel
+        "fwd": ("mfma", 4.0 * d * pairs),            # S = QK^T and O += PV
+        "bwd_dkdv": ("mfma", 8.0 * d * pairs),       # S, dP, dV += P^T dO, dK += dS^T Q
+        "bwd_dq": ("mfma", 6.0 * d * pairs),         # S, dP, dQ += dS K
+        "bwd_preprocess": ("hbm", 2.0 * B * N * H * d * 2 + 4.0 * B * H * N),   # read O, dO; write D
+    }
+    dom = max(avg, key=avg.get)
+    bound, work = alg[dom]
+    if bound == "mfma":
+        achieved = work / (avg[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        achieved = work / (avg[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(achieved / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = round(avg[dom], 4)
+    roof["algorithmic_per_launch"] = work
+    roof["traffic"] = kernel_traffic(dom)
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fwd+bwd causal bf16 [B,N,H,d]=[2,8192,16,64], scale 1/8, seeded N(0,1)",
+                   "B": B, "N": N, "H": H, "d": d, "causal": True, "scale": w.scale},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "breakdown": {
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "fwd_tflops": round(F / (fwd_ms * 1e-3) / 1e12, 1),
+            "bwd_tflops_credited": round(Fb / (bwd_ms * 1e-3) / 1e12, 1),
+            "fwd_pct_of_peak": round(100 * F / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "bwd_pct_of_peak_credited": round(100 * Fb / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "kernel_avg_ms": {n: round(x, 4) for n, x in avg.items()},
+        },
+    }
+
+    if not args.no_extra:
+        log("bench: forward-only long causal workloads")
+        result["forward_only"] = {
+            "c3_causal": time_forward_only(fa, torch, 4, 4096, 16, 128, synth.f32(128 ** -0.5), 1.0, 3, 20),
+            "c4": time_forward_only(fa, torch, 1, 32768, 32, 128, synth.f32(128 ** -0.5), 2.0, 4, 10),
+        }
+
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline on one head")
+        got = {"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv}
+        result["cpu_baseline"], result["sample_parity_max_abs_err"] = cpu_baseline(w, host, got)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,8 +13,9 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_workspace_bytes,  # noqa: F401
-                   fa_forward, fa_status_string, load)
+from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_dkdv, fa_backward_dq,  # noqa: F401
+                   fa_backward_preprocess, fa_backward_workspace_bytes, fa_forward,
+                   fa_status_string, load)
 
 
 def _scale(q, scale):

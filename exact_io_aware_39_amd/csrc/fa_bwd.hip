@@ -375,33 +375,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int D>
-hipError_t run(const BwdArgs& a0, int B, int BH, bool causal, hipStream_t st) {
-  const int64_t rows = (int64_t)B * a0.N * a0.H;
+hipError_t run_pre(const BwdArgs& a, int B, hipStream_t st) {
+  const int64_t rows = (int64_t)B * a.N * a.H;
   const int64_t threads = rows * (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                     a0.o, a0.dout, a0.dvec_out, a0.H, a0.N, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  BwdArgs a = a0;
-  a.ntiles = (a.N + kKeysPerWg - 1) / kKeysPerWg;
-  const dim3 g1(a.ntiles * BH);
-  if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), g1, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), g1, dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-
-  a.ntiles = (a.N + kQPerWg - 1) / kQPerWg;
-  const dim3 g2(a.ntiles * BH);
-  if (causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), g2, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), g2, dim3(256), 0, st, a);
+                     a.o, a.dout, a.dvec_out, a.H, a.N, rows);
   return hipGetLastError();
 }
 
-}  // namespace
+template <int D>
+hipError_t run_dkdv(BwdArgs a, int BH, bool causal, hipStream_t st) {
+  a.ntiles = (a.N + kKeysPerWg - 1) / kKeysPerWg;
+  const dim3 grid(a.ntiles * BH);
+  if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
-                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           float* dvec, const AttnShape& s, hipStream_t stream) {
+template <int D>
+hipError_t run_dq(BwdArgs a, int BH, bool causal, hipStream_t st) {
+  a.ntiles = (a.N + kQPerWg - 1) / kQPerWg;
+  const dim3 grid(a.ntiles * BH);
+  if (causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+BwdArgs make_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, const float* dvec_in, float* dvec_out, void* dq, void* dk,
+                  void* dv, const AttnShape& s) {
   BwdArgs a{};
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
@@ -409,8 +411,8 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   a.o = static_cast<const __bf16*>(o);
   a.dout = static_cast<const __bf16*>(dout);
   a.lse = lse;
-  a.dvec = dvec;
-  a.dvec_out = dvec;
+  a.dvec = dvec_in;
+  a.dvec_out = dvec_out;
   a.dq = static_cast<__bf16*>(dq);
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
@@ -418,9 +420,43 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   a.N = s.N;
   a.c = s.scale * kLog2e;
   a.scale = s.scale;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_pre_bf16(const void* o, const void* dout, float* dvec, const AttnShape& s,
+                               hipStream_t stream) {
+  const BwdArgs a = make_args(nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, dvec, nullptr,
+                              nullptr, nullptr, s);
+  return s.d == 64 ? run_pre<64>(a, s.B, stream) : run_pre<128>(a, s.B, stream);
+}
+
+hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout,
+                                const float* lse, const float* dvec, void* dk, void* dv,
+                                const AttnShape& s, hipStream_t stream) {
+  const BwdArgs a = make_args(q, k, v, nullptr, dout, lse, dvec, nullptr, nullptr, dk, dv, s);
   const int BH = s.B * s.H;
-  return s.d == 64 ? run<64>(a, s.B, BH, s.causal != 0, stream)
-                   : run<128>(a, s.B, BH, s.causal != 0, stream);
+  return s.d == 64 ? run_dkdv<64>(a, BH, s.causal != 0, stream)
+                   : run_dkdv<128>(a, BH, s.causal != 0, stream);
+}
+
+hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout,
+                              const float* lse, const float* dvec, void* dq, const AttnShape& s,
+                              hipStream_t stream) {
+  const BwdArgs a = make_args(q, k, v, nullptr, dout, lse, dvec, nullptr, dq, nullptr, nullptr, s);
+  const int BH = s.B * s.H;
+  return s.d == 64 ? run_dq<64>(a, BH, s.causal != 0, stream)
+                   : run_dq<128>(a, BH, s.causal != 0, stream);
+}
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           float* dvec, const AttnShape& s, hipStream_t stream) {
+  hipError_t e = launch_bwd_pre_bf16(o, dout, dvec, s, stream);
+  if (e == hipSuccess) e = launch_bwd_dkdv_bf16(q, k, v, dout, lse, dvec, dk, dv, s, stream);
+  if (e == hipSuccess) e = launch_bwd_dq_bf16(q, k, v, dout, lse, dvec, dq, s, stream);
+  return e;
 }
 
 }  // namespace fa

@@ -95,6 +95,25 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
                       const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
                       int B, int H, int N, int d, float scale, int causal, void* stream);
 
+/*
+ * The three passes fa_backward runs, in this order, for callers that schedule
+ * them themselves (bf16 tensors, same layouts and checks as fa_backward):
+ *   fa_backward_preprocess  workspace[b, h, i] = D_i = sum_c dO_ic O_ic (fp32);
+ *   fa_backward_dkdv        dK = scale dS^T Q and dV = P^T dO, reading D from
+ *                           `workspace` (written by the preprocess);
+ *   fa_backward_dq          dQ = scale dS K, reading D from `workspace`.
+ * The dK/dV and dQ passes only read shared inputs, so once the preprocess has
+ * completed they may run concurrently on different streams.
+ */
+fa_status fa_backward_preprocess(const void* O, const void* dO, float* workspace,
+                                 int B, int H, int N, int d, void* stream);
+fa_status fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                           const float* LSE, const float* workspace, void* dK, void* dV,
+                           int B, int H, int N, int d, float scale, int causal, void* stream);
+fa_status fa_backward_dq(const void* Q, const void* K, const void* V, const void* dO,
+                         const float* LSE, const float* workspace, void* dQ,
+                         int B, int H, int N, int d, float scale, int causal, void* stream);
+
 /* Backward, float32 tensors: same contract as fa_backward, every tensor fp32. */
 fa_status fa_backward_f32(const float* Q, const float* K, const float* V, const float* O,
                           const float* dO, const float* LSE, float* dQ, float* dK, float* dV,

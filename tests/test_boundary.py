@@ -36,6 +36,12 @@ def lib():
     for name in ("fa_backward", "fa_backward_f32"):
         getattr(lib, name).argtypes = [vp] * 10 + [i] * 4 + [f, i, vp]
         getattr(lib, name).restype = i
+    lib.fa_backward_preprocess.argtypes = [vp] * 3 + [i] * 4 + [vp]
+    lib.fa_backward_preprocess.restype = i
+    lib.fa_backward_dkdv.argtypes = [vp] * 8 + [i] * 4 + [f, i, vp]
+    lib.fa_backward_dkdv.restype = i
+    lib.fa_backward_dq.argtypes = [vp] * 7 + [i] * 4 + [f, i, vp]
+    lib.fa_backward_dq.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i] * 4
     lib.fa_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
@@ -46,6 +52,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_f32",
+        "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq",
         "fa_backward_workspace_bytes", "fa_status_string"])
 
 
@@ -104,6 +111,31 @@ def test_backward_rejects_bad_arguments(lib, name):
         ptrs = [P] * 10
         ptrs[i] = P + 2
         assert _bwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+
+
+def test_backward_passes_reject_bad_arguments(lib):
+    assert lib.fa_backward_preprocess(P, P, P, 1, 1, 128, 96, None) == UNSUPPORTED
+    assert lib.fa_backward_preprocess(P, P, P, 1, 0, 128, 64, None) == INVALID
+    for i in range(3):
+        ptrs = [P] * 3
+        ptrs[i] = None
+        assert lib.fa_backward_preprocess(*ptrs, 1, 1, 128, 64, None) == INVALID
+    assert lib.fa_backward_preprocess(P + 8, P, P, 1, 1, 128, 64, None) == INVALID
+    assert lib.fa_backward_preprocess(P, P, P + 2, 1, 1, 128, 64, None) == INVALID
+    for name, n in (("fa_backward_dkdv", 8), ("fa_backward_dq", 7)):
+        fn = getattr(lib, name)
+        assert fn(*([P] * n), 1, 1, 128, 32, 0.1, 0, None) == UNSUPPORTED
+        assert fn(*([P] * n), 1, 1, 128, 64, float("nan"), 0, None) == INVALID
+        assert fn(*([P] * n), 1, 1, 128, 64, 0.1, 5, None) == INVALID
+        for i in range(n):
+            ptrs = [P] * n
+            ptrs[i] = None
+            assert fn(*ptrs, 1, 1, 128, 64, 0.1, 1, None) == INVALID
+        stats = (4, 5)                       # LSE and workspace come 5th and 6th
+        for i in range(n):
+            ptrs = [P] * n
+            ptrs[i] = P + (2 if i in stats else 8)
+            assert fn(*ptrs, 1, 1, 128, 64, 0.1, 1, None) == INVALID
 
 
 def test_workspace_bytes(lib):
