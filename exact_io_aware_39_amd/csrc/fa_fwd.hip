@@ -30,6 +30,8 @@
 //    diagonal (or the ragged end of the keys) evaluate the mask.
 //  * Workgroups are renumbered per XCD so one head's query tiles share an L2,
 //    and causal query tiles run heaviest first.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -56,9 +58,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int KS = D / 16;           // k-steps of the score product
   constexpr int DT = D / 32;           // 32-wide output tiles
-  constexpr int TILE = kBc * D * 2;    // bytes of one K or V tile
-  constexpr int CPT = kBc * CH / 256;  // chunks each thread stages per tile
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+  // Padded LDS rows: K rows are read 16 bytes at a time, 16 rows at one
+  // column (a 16-byte pad puts those rows in 16 different bank groups); V rows
+  // are read by the transposing 8-byte read, 4 rows x 64 bytes per half-wave
+  // (a 64-byte pad puts those rows in 4 disjoint quarters of the banks).
+  // Offsets stay additive, so every fragment address is a lane base plus an
+  // immediate.
+  constexpr int KSTR = D * 2 + 16;       // bytes per K row in LDS
+  constexpr int VSTR = D * 2 + 64;       // bytes per V row in LDS
+  constexpr int KT = kBc * KSTR;         // bytes of one K tile
+  constexpr int STAGE = KT + kBc * VSTR; // K tile then V tile
+  constexpr int CPT = kBc * CH / 256;    // chunks each thread stages per tile
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -91,29 +102,55 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int kend = CAUSAL ? min(N, q0 + kBr) : N;
   const int nkt = (kend + kBc - 1) / kBc;
 
+  // Global offsets (elements) of the chunks this thread stages, for key tile 0.
+  int64_t goff[CPT];
+  int grow[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int idx = tid + 256 * i;
+    grow[i] = idx / CH;
+    goff[i] = (int64_t)grow[i] * rs + (idx % CH) * 8;
+  }
+  const int64_t tile_step = (int64_t)kBc * rs;
   u32x4 kreg[CPT], vreg[CPT];
   auto gload = [&](int kt) {
+    const int64_t t0 = kt * tile_step;
+    if (kt * kBc + kBc <= N) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / CH, ch = idx % CH;
-      const int64_t key = min(kt * kBc + row, N - 1);   // rows past N: real, finite data
-      kreg[i] = *reinterpret_cast<const u32x4*>(Kg + key * rs + ch * 8);
-      vreg[i] = *reinterpret_cast<const u32x4*>(Vg + key * rs + ch * 8);
+      for (int i = 0; i < CPT; ++i) {
+        kreg[i] = *reinterpret_cast<const u32x4*>(Kg + t0 + goff[i]);
+        vreg[i] = *reinterpret_cast<const u32x4*>(Vg + t0 + goff[i]);
+      }
+    } else {   // ragged last tile: rows past N re-read row N-1 (real, finite data)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int over = kt * kBc + grow[i] - (N - 1);
+        const int64_t off = t0 + goff[i] - (over > 0 ? (int64_t)over * rs : 0);
+        kreg[i] = *reinterpret_cast<const u32x4*>(Kg + off);
+        vreg[i] = *reinterpret_cast<const u32x4*>(Vg + off);
+      }
     }
   };
+  // Staging: thread tid writes chunk (row, ch) of each tile; the row steps by
+  // 256 / CH between its chunks.
+  const uint32_t kst = (tid / CH) * KSTR + (tid % CH) * 16;
+  const uint32_t vst = (tid / CH) * VSTR + (tid % CH) * 16;
   auto swrite = [&](int stage) {
-    char* kb = smem + stage * 2 * TILE;
-    char* vb = kb + TILE;
+    char* kb = smem + stage * STAGE;
+    char* vb = kb + KT;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / CH, ch = idx % CH;
-      const uint32_t off = tile_off<D>(row, ch);
-      *reinterpret_cast<u32x4*>(kb + off) = kreg[i];
-      *reinterpret_cast<u32x4*>(vb + off) = vreg[i];
+      *reinterpret_cast<u32x4*>(kb + kst + i * (256 / CH) * KSTR) = kreg[i];
+      *reinterpret_cast<u32x4*>(vb + vst + i * (256 / CH) * VSTR) = vreg[i];
     }
   };
+  // Lane bases of the fragment reads (the rest of each address is constant).
+  //  K (A operand of S^T): row 32 j + l%32, chunk 2 ks + l/32.
+  const uint32_t kfrag = l32 * KSTR + hh * 16;
+  //  V^T (A operand of O^T) through the transposing read: within each group of
+  //  16 lanes, lane i addresses row 4 (l/32) + i/4 and column 16 ((l/16)%2) + 4 (i%4).
+  const int ti = lane & 15, tg = lane >> 4;
+  const uint32_t vfrag = ((tg >> 1) * 4 + (ti >> 2)) * VSTR + ((tg & 1) * 16 + (ti & 3) * 4) * 2;
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -121,6 +158,70 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   float m_ref = -INFINITY;   // reference max, log2 units
   float l_part = 0.f;        // this half-wave's share of the row sum
   const float c = a.c;
+
+  // Softmax update and O^T += V^T P^T for one step; MASK evaluates the causal /
+  // ragged-end mask, the common path carries no per-element test.
+  auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[2], const char* vb, int k0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    float mx = -INFINITY;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool hide = key >= N || (CAUSAL && key > myq);
+          s[j][r] = hide ? -INFINITY : s[j][r];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+    mx = max_halves(mx);
+    const float mcand = MASK ? ((mx == -INFINITY) ? -INFINITY : mx * c) : mx * c;
+    const float m_new = fmaxf(m_ref, mcand);
+    if (__any(m_new > m_ref + kRescaleLog2)) {
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float nm = -m_ref;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = fast_exp2(__builtin_fmaf(s[j][r], c, nm));
+        if constexpr (MASK) e = (s[j][r] == -INFINITY) ? 0.f : e;
+        p[r] = e;
+        l_part += e;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        pb[j][u] = pack_bf16x8(p[8 * u + 0], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3],
+                               p[8 * u + 4], p[8 * u + 5], p[8 * u + 6], p[8 * u + 7]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          const uint32_t off = vfrag + (32 * j + 16 * u) * VSTR + t * 64;
+          const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_read_tr16(vb, off));
+          const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_read_tr16(vb, off + 8 * VSTR));
+          bf16x8 va;
+          va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
+          va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
+          oacc[t] = mfma32x32x16(va, pb[j][u], oacc[t]);
+        }
+  };
 
   gload(0);
   for (int kt = 0; kt < nkt; ++kt) {
@@ -133,92 +234,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     // All keys of this step lie beyond this wave's rows: nothing to add.
     if (CAUSAL && k0 > qw0 + 31) continue;
 
-    const char* kb = smem + stage * 2 * TILE;
-    const char* vb = kb + TILE;
+    const char* kb = smem + stage * STAGE;
+    const char* vb = kb + KT;
 
-    // ---- S^T = K Q^T for two 32-key sub-tiles
-    f32x16 s[2];
+    // ---- S^T = K Q^T for two 32-key sub-tiles (independent chains interleaved)
+    f32x16 s[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      s[j] = (f32x16){};
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = lds_read_b128(kb, tile_off<D>(32 * j + l32, 2 * ks + hh));
-        s[j] = mfma32x32x16(kf, qf[ks], s[j]);
-      }
-    }
+      for (int j = 0; j < 2; ++j)
+        s[j] = mfma32x32x16(lds_read_b128(kb, kfrag + 32 * j * KSTR + 32 * ks), qf[ks], s[j]);
 
     const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
-    float mx = -INFINITY;
-    if (masked) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool hide = key >= N || (CAUSAL && key > myq);
-          s[j][r] = hide ? -INFINITY : s[j][r];
-          mx = fmaxf(mx, s[j][r]);
-        }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
-    }
-    mx = max_halves(mx);
-    const float mcand = (mx == -INFINITY) ? -INFINITY : mx * c;
-    const float m_new = fmaxf(m_ref, mcand);
-    if (__any(m_new > m_ref + kRescaleLog2)) {
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-      m_ref = m_new;
-    }
-
-    // ---- P = exp2(c S - m_ref); masked entries are exactly 0.
-    const float nm = -m_ref;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(s[j][r], c, nm));
-        p[r] = (masked && s[j][r] == -INFINITY) ? 0.f : e;
-        l_part += p[r];
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        pb[j][u] = pack_bf16x8(p[8 * u + 0], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3],
-                               p[8 * u + 4], p[8 * u + 5], p[8 * u + 6], p[8 * u + 7]);
-    }
-
-    // ---- O^T += V^T P^T
-    {
-      const int i = lane & 15, g = lane >> 4;
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const int col = t * 32 + (g & 1) * 16 + (i & 3) * 4;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int row = 32 * j + 16 * u + (g >> 1) * 4 + (i >> 2);
-            const s16x4 lo = lds_read_tr16(vb, elem_off<D>(row, col));
-            const s16x4 hi = lds_read_tr16(vb, elem_off<D>(row + 8, col));
-            bf16x8 va;
-            const bf16x4 lo4 = __builtin_bit_cast(bf16x4, lo);
-            const bf16x4 hi4 = __builtin_bit_cast(bf16x4, hi);
-            va[0] = lo4[0]; va[1] = lo4[1]; va[2] = lo4[2]; va[3] = lo4[3];
-            va[4] = hi4[0]; va[5] = hi4[1]; va[6] = hi4[2]; va[7] = hi4[3];
-            oacc[t] = mfma32x32x16(va, pb[j][u], oacc[t]);
-          }
-      }
-    }
+    if (masked) softmax_pv(std::true_type{}, s, vb, k0);
+    else softmax_pv(std::false_type{}, s, vb, k0);
   }
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
