@@ -28,6 +28,9 @@ fa_status check_common(int B, int H, int N, int d, float scale, int causal) {
   const int64_t bh = (int64_t)B * H;
   if (bh > (1 << 20)) return FA_ERR_UNSUPPORTED;
   if (bh * N * d >= ((int64_t)1 << 40)) return FA_ERR_UNSUPPORTED;
+  // K/V tiles are staged through buffer descriptors whose 32-bit offsets span
+  // 64 rows of the [B, N, H, d] tensors.
+  if ((int64_t)H * d > (1 << 24)) return FA_ERR_UNSUPPORTED;
   // The largest grid any kernel uses: one workgroup per 64 rows of each head.
   if (bh * ((N + 63) / 64) > INT_MAX) return FA_ERR_UNSUPPORTED;
   return FA_OK;

@@ -42,12 +42,8 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value of x held by lane (l + 32) % 64, i.e. the other half of the wave.
-__device__ __forceinline__ float other_half(float x) {
-  const int lane = __lane_id();
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(lane < 32 ? r[1] : r[0]);
-}
+// Combine x with the value held by lane (l + 32) % 64 (v_permlane32_swap
+// exchanges the two half-waves; both results are symmetric in the pair).
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -115,6 +111,28 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, uint32_t off) 
 __device__ __forceinline__ s16x4 lds_read_tr16(const char* base, uint32_t off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + off));
 }
+
+// Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l's
+// 16 bytes from `src` land at lds_block + 16 l.  `lds_block` must be the same
+// for every lane of the wave.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void global_to_lds16(const void* src, void* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)lds_block, 16, 0, 0);
+}
+
+// Buffer descriptor over `bytes` bytes from `base` (raw, unswizzled dwords);
+// loads at offsets >= bytes return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Asynchronous 16-byte buffer -> LDS copy: lane l's 16 bytes at byte offset
+// `voff` of the buffer land at lds_block + 16 l (lds_block wave-uniform).
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds_block, 16, voff, 0, 0, 0);
+}
+
+// Wait until this wave's global loads (including global -> LDS copies) are done.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
 // XCD runs one contiguous range of logical tiles (neighbouring tiles share the

@@ -17,9 +17,14 @@
 //  * The fp32 S^T accumulator, exponentiated and rounded to bf16, is directly
 //    the B operand of O^T += V^T P^T: no LDS round trip for P.
 //  * V^T fragments come from row-major V tiles in LDS through the transposing
-//    read ds_read_b64_tr_b16; K fragments are plain 16-byte LDS reads.
-//  * K/V tiles are double buffered in LDS; the next tile's global loads are in
-//    flight during the current tile's matrix work; one barrier per step.
+//    read ds_read_b64_tr_b16; K fragments are plain 16-byte LDS reads.  Tile
+//    rows are dense with XOR-permuted 16-byte chunks (no bank conflicts for
+//    either read); every fragment address is a lane base XOR a constant.
+//  * K and V tiles are double buffered in LDS and filled by asynchronous
+//    global -> LDS copies (no staging registers); K runs one tile ahead of V
+//    so that step t issues the score product of tile t+1 before the softmax of
+//    tile t (software pipelining: the MFMA latency of S hides under the exp
+//    work) and then tile t's P V product; one barrier per step.
 //  * exp is exp2 with scale*log2(e) folded into one FMA.  The reference max is
 //    only moved when a row's max grows by more than 2^8 (RESCALE_LOG2): any
 //    finite reference gives the same O and LSE (the final divide uses the same
@@ -42,6 +47,7 @@ constexpr int kWaves = 4;
 constexpr int kBr = 32 * kWaves;   // query rows per workgroup
 constexpr int kBc = 64;            // keys per step
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kSumLimit = 65536.0f;
 
 struct FwdArgs {
   const __bf16* q;
@@ -58,18 +64,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int KS = D / 16;           // k-steps of the score product
   constexpr int DT = D / 32;           // 32-wide output tiles
-  // Padded LDS rows: K rows are read 16 bytes at a time, 16 rows at one
-  // column (a 16-byte pad puts those rows in 16 different bank groups); V rows
-  // are read by the transposing 8-byte read, 4 rows x 64 bytes per half-wave
-  // (a 64-byte pad puts those rows in 4 disjoint quarters of the banks).
-  // Offsets stay additive, so every fragment address is a lane base plus an
-  // immediate.
-  constexpr int KSTR = D * 2 + 16;       // bytes per K row in LDS
-  constexpr int VSTR = D * 2 + 64;       // bytes per V row in LDS
-  constexpr int KT = kBc * KSTR;         // bytes of one K tile
-  constexpr int STAGE = KT + kBc * VSTR; // K tile then V tile
-  constexpr int CPT = kBc * CH / 256;    // chunks each thread stages per tile
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  constexpr int RB = D * 2;            // bytes per LDS row (dense, chunks swizzled)
+  constexpr int TILE = kBc * RB;       // bytes of one K or V tile
+  constexpr int CPW = TILE / 1024 / kWaves;   // 1 KB global->LDS copies per wave per tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];   // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -102,55 +100,47 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int kend = CAUSAL ? min(N, q0 + kBr) : N;
   const int nkt = (kend + kBc - 1) / kBc;
 
-  // Global offsets (elements) of the chunks this thread stages, for key tile 0.
-  int64_t goff[CPT];
-  int grow[CPT];
+  // Staging: copy i of this wave fills LDS block (wave + 4 i) of a tile; lane
+  // l's 16 bytes are physical chunk slot%CH of row slot/CH (slot = 64 block + l),
+  // which holds logical chunk (slot%CH) ^ swz(row) of that key row.  The copies
+  // go through a buffer descriptor that covers exactly the valid rows of the
+  // tile, so rows past N read as zeros (they are masked anyway); the per-lane
+  // byte offsets are the same for every tile.
+  uint32_t svoff[CPW];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int idx = tid + 256 * i;
-    grow[i] = idx / CH;
-    goff[i] = (int64_t)grow[i] * rs + (idx % CH) * 8;
+  for (int i = 0; i < CPW; ++i) {
+    const int slot = (wave + kWaves * i) * 64 + lane;
+    const int row = slot / CH;
+    svoff[i] = (uint32_t)(row * rs * 2) + (uint32_t)(((slot % CH) ^ swz<D>(row)) * 16);
   }
-  const int64_t tile_step = (int64_t)kBc * rs;
-  u32x4 kreg[CPT], vreg[CPT];
-  auto gload = [&](int kt) {
-    const int64_t t0 = kt * tile_step;
-    if (kt * kBc + kBc <= N) {
+  // LDS: two K buffers and two V buffers.  Step t reads K of tile t+1 (for the
+  // next score product) and V of tile t, while tile t+2's K and tile t+1's V
+  // are copied into the other buffers.
+  char* const kbuf = smem;
+  char* const vbuf = smem + 2 * TILE;
+  auto stage_rows = [&](const __bf16* src, int kt, char* dst) {
+    const int rows = min(N - kt * kBc, kBc);
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src + (int64_t)kt * kBc * rs, (uint32_t)(rows * rs * 2));
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kg + t0 + goff[i]);
-        vreg[i] = *reinterpret_cast<const u32x4*>(Vg + t0 + goff[i]);
-      }
-    } else {   // ragged last tile: rows past N re-read row N-1 (real, finite data)
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int over = kt * kBc + grow[i] - (N - 1);
-        const int64_t off = t0 + goff[i] - (over > 0 ? (int64_t)over * rs : 0);
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kg + off);
-        vreg[i] = *reinterpret_cast<const u32x4*>(Vg + off);
-      }
-    }
+    for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, svoff[i], dst + (wave + kWaves * i) * 1024);
   };
-  // Staging: thread tid writes chunk (row, ch) of each tile; the row steps by
-  // 256 / CH between its chunks.
-  const uint32_t kst = (tid / CH) * KSTR + (tid % CH) * 16;
-  const uint32_t vst = (tid / CH) * VSTR + (tid % CH) * 16;
-  auto swrite = [&](int stage) {
-    char* kb = smem + stage * STAGE;
-    char* vb = kb + KT;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      *reinterpret_cast<u32x4*>(kb + kst + i * (256 / CH) * KSTR) = kreg[i];
-      *reinterpret_cast<u32x4*>(vb + vst + i * (256 / CH) * VSTR) = vreg[i];
-    }
-  };
-  // Lane bases of the fragment reads (the rest of each address is constant).
-  //  K (A operand of S^T): row 32 j + l%32, chunk 2 ks + l/32.
-  const uint32_t kfrag = l32 * KSTR + hh * 16;
-  //  V^T (A operand of O^T) through the transposing read: within each group of
-  //  16 lanes, lane i addresses row 4 (l/32) + i/4 and column 16 ((l/16)%2) + 4 (i%4).
-  const int ti = lane & 15, tg = lane >> 4;
-  const uint32_t vfrag = ((tg >> 1) * 4 + (ti >> 2)) * VSTR + ((tg & 1) * 16 + (ti & 3) * 4) * 2;
+
+  // Lane bases of the fragment reads.  The chunk field of an address (bits
+  // 4 .. 4+log2(CH)-1) is zero in the row part, so swizzled addresses are the
+  // lane base XOR a per-read constant, plus an immediate row offset.
+  //  K (A operand of S^T): row 32 j + l%32, logical chunk 2 ks + l/32.
+  const uint32_t kl = (uint32_t)(l32 * RB) | ((uint32_t)(hh ^ swz<D>(l32)) << 4);
+  //  V^T (A operand of O^T), transposing read: within each group of 16 lanes,
+  //  lane i addresses row 32 j + 16 u + r4 (+8 for the high half), r4 =
+  //  4 (l/32) + i/4, and element column 32 t + 16 ((l/16)%2) + 4 (i%4).
+  uint32_t vl;
+  {
+    const int ti = lane & 15, tg = lane >> 4;
+    const int r4 = (tg >> 1) * 4 + (ti >> 2);
+    const int cl = (tg & 1) * 2 + ((ti & 3) >> 1);
+    const int sw0 = swz<D>(r4);
+    vl = (uint32_t)(r4 * RB) | ((uint32_t)(cl ^ sw0) << 4) | ((uint32_t)(ti & 1) << 3);
+  }
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -159,11 +149,59 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   float l_part = 0.f;        // this half-wave's share of the row sum
   const float c = a.c;
 
-  // Softmax update and O^T += V^T P^T for one step; MASK evaluates the causal /
-  // ragged-end mask, the common path carries no per-element test.
+  // Moves the reference max to the exact running max of the rows (in log2
+  // units) and rescales the running sum and output to it.
+  auto move_reference = [&](f32x16 (&s)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m_ref, (mx == -INFINITY) ? -INFINITY : mx * c);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
+    l_part *= alpha;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+    m_ref = m_new;
+  };
+
+  // P = exp2(c S - m_ref) for one step, its row-sum share, and bf16 operands.
+  auto exp_tile = [&](auto mask_tag, const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const float nm = -m_ref;
+    float lsum[2] = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = fast_exp2(__builtin_fmaf(s[j][r], c, nm));
+        if constexpr (MASK) e = (s[j][r] == -INFINITY) ? 0.f : e;
+        p[r] = e;
+        lsum[r & 1] += e;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        pb[j][u] = pack_bf16x8(p[8 * u + 0], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3],
+                               p[8 * u + 4], p[8 * u + 5], p[8 * u + 6], p[8 * u + 7]);
+    }
+    return lsum[0] + lsum[1];
+  };
+
+  // Softmax update and O^T += V^T P^T for one step.
+  //  MASK steps (diagonal or ragged end) hide keys and move the reference to
+  //  the exact running max when it grows by more than 2^8.
+  //  Other steps exponentiate against the current reference straight away and
+  //  only look at the row max (and redo the step) if some row's share of the
+  //  sum exceeds 2^16, which bounds every probability by 2^16; the reference
+  //  is -inf before the first step, so the first step always takes that path.
   auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[2], const char* vb, int k0) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    float mx = -INFINITY;
+    bf16x8 pb[2][2];
+    float lsum;
     if constexpr (MASK) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -173,49 +211,32 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
           const bool hide = key >= N || (CAUSAL && key > myq);
           s[j][r] = hide ? -INFINITY : s[j][r];
         }
-    }
+      float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
-    mx = max_halves(mx);
-    const float mcand = MASK ? ((mx == -INFINITY) ? -INFINITY : mx * c) : mx * c;
-    const float m_new = fmaxf(m_ref, mcand);
-    if (__any(m_new > m_ref + kRescaleLog2)) {
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-      m_ref = m_new;
-    }
-    const float nm = -m_ref;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = fast_exp2(__builtin_fmaf(s[j][r], c, nm));
-        if constexpr (MASK) e = (s[j][r] == -INFINITY) ? 0.f : e;
-        p[r] = e;
-        l_part += e;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+      mx = max_halves(mx);
+      const float mcand = (mx == -INFINITY) ? -INFINITY : mx * c;
+      if (__any(fmaxf(m_ref, mcand) > m_ref + kRescaleLog2)) move_reference(s);
+      lsum = exp_tile(std::true_type{}, s, pb);
+    } else {
+      lsum = exp_tile(std::false_type{}, s, pb);
+      if (__any(!(lsum <= kSumLimit))) {
+        move_reference(s);
+        lsum = exp_tile(std::false_type{}, s, pb);
       }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        pb[j][u] = pack_bf16x8(p[8 * u + 0], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3],
-                               p[8 * u + 4], p[8 * u + 5], p[8 * u + 6], p[8 * u + 7]);
     }
+    l_part += lsum;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-          const uint32_t off = vfrag + (32 * j + 16 * u) * VSTR + t * 64;
-          const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_read_tr16(vb, off));
-          const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_read_tr16(vb, off + 8 * VSTR));
+          const uint32_t rowoff = (32 * j + 16 * u) * RB;
+          const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_read_tr16(vb, (vl ^ (64 * t)) + rowoff));
+          const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_read_tr16(vb, (vl ^ (64 * t + 32)) + rowoff + 8 * RB));
           bf16x8 va;
           va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
           va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
@@ -223,32 +244,56 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
         }
   };
 
-  gload(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int stage = kt & 1;
-    swrite(stage);
-    __syncthreads();
-    if (kt + 1 < nkt) gload(kt + 1);
-
-    const int k0 = kt * kBc;
-    // All keys of this step lie beyond this wave's rows: nothing to add.
-    if (CAUSAL && k0 > qw0 + 31) continue;
-
-    const char* kb = smem + stage * STAGE;
-    const char* vb = kb + KT;
-
-    // ---- S^T = K Q^T for two 32-key sub-tiles (independent chains interleaved)
-    f32x16 s[2] = {(f32x16){}, (f32x16){}};
+  // S^T = K Q^T for the two 32-key sub-tiles of a K buffer (independent
+  // accumulation chains interleaved).
+  auto scores = [&](const char* kb, f32x16 (&s)[2]) {
+    s[0] = (f32x16){};
+    s[1] = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        s[j] = mfma32x32x16(lds_read_b128(kb, kfrag + 32 * j * KSTR + 32 * ks), qf[ks], s[j]);
+        s[j] = mfma32x32x16(lds_read_b128(kb, (kl ^ (ks << 5)) + 32 * j * RB), qf[ks], s[j]);
+  };
 
+  // Software pipeline: the score product of tile t+1 is issued before the
+  // softmax of tile t, so the matrix cores work on it while the vector unit
+  // exponentiates; tile t's P V product follows.
+  // One step: copies for later tiles, next tile's scores into `snext`, then
+  // softmax and P V of tile kt from `scur`.
+  auto step = [&](int kt, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+    wait_vmem();
+    __syncthreads();
+    if (kt + 2 < nkt) stage_rows(Kg, kt + 2, kbuf + (kt & 1) * TILE);
+    if (kt + 1 < nkt) stage_rows(Vg, kt + 1, vbuf + ((kt + 1) & 1) * TILE);
+    const int k0 = kt * kBc;
+    // All keys of this step lie beyond this wave's rows: nothing left to add.
+    if (CAUSAL && k0 > qw0 + 31) return;
+    // Scores of the next tile (on the last step this reads a stale buffer and
+    // the result is never used).
+    scores(kbuf + ((kt + 1) & 1) * TILE, snext);
+    const char* vb = vbuf + (kt & 1) * TILE;
     const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
-    if (masked) softmax_pv(std::true_type{}, s, vb, k0);
-    else softmax_pv(std::false_type{}, s, vb, k0);
+    if (masked) softmax_pv(std::true_type{}, scur, vb, k0);
+    else softmax_pv(std::false_type{}, scur, vb, k0);
+  };
+
+  // Software pipeline: the score product of tile t+1 is issued before the
+  // softmax of tile t, so the matrix cores work on it while the vector unit
+  // exponentiates; tile t's P V product follows.
+  stage_rows(Kg, 0, kbuf);
+  stage_rows(Vg, 0, vbuf);
+  if (nkt > 1) stage_rows(Kg, 1, kbuf + TILE);
+  wait_vmem();
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  scores(kbuf, sa);
+  int kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
+    step(kt, sa, sb);
+    step(kt + 1, sb, sa);
   }
+  if (kt < nkt) step(kt, sa, sb);
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
   const float l = sum_halves(l_part);

@@ -47,7 +47,7 @@
  *                                   fallback path;
  *               FA_ERR_LAUNCH       a HIP call or kernel launch failed.
  *             On error nothing has been enqueued.
- *   Limits    N <= 2^20, B*H <= 2^20, B*N*H*d < 2^40 elements.
+ *   Limits    N <= 2^20, B*H <= 2^20, H*d <= 2^24, B*N*H*d < 2^40 elements.
  */
 #ifndef FA_H_
 #define FA_H_

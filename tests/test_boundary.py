@@ -77,6 +77,7 @@ def test_forward_rejects_bad_arguments(lib, name):
         assert _fwd(lib, name, B=B, H=H, N=N) == INVALID
     assert _fwd(lib, name, N=(1 << 20) + 1) == UNSUPPORTED
     assert _fwd(lib, name, B=1 << 11, H=1 << 10) == UNSUPPORTED
+    assert _fwd(lib, name, H=(1 << 17) + 1, d=128) == UNSUPPORTED
     for s in (float("nan"), float("inf"), float("-inf")):
         assert _fwd(lib, name, scale=s) == INVALID
     assert _fwd(lib, name, scale=-0.5) == UNSUPPORTED
