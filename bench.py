@@ -181,13 +181,13 @@ def main():
         fa.fa_forward(q, k, v, o, lse, w.scale, True)
         if evs:
             evs[1].record(st)
-        fa.fa_backward_preprocess(o, do, ws)
+        fa.fa_backward_preprocess(o, do, lse, ws)
         if evs:
             evs[2].record(st)
-        fa.fa_backward_dkdv(q, k, v, do, lse, ws, dk, dv, w.scale, True)
+        fa.fa_backward_dkdv(q, k, v, do, ws, dk, dv, w.scale, True)
         if evs:
             evs[3].record(st)
-        fa.fa_backward_dq(q, k, v, do, lse, ws, dq, w.scale, True)
+        fa.fa_backward_dq(q, k, v, do, ws, dq, w.scale, True)
         if evs:
             evs[4].record(st)
 
@@ -215,7 +215,7 @@ def main():
         "fwd": ("mfma", 4.0 * d * pairs),            # S = QK^T and O += PV
         "bwd_dkdv": ("mfma", 8.0 * d * pairs),       # S, dP, dV += P^T dO, dK += dS^T Q
         "bwd_dq": ("mfma", 6.0 * d * pairs),         # S, dP, dQ += dS K
-        "bwd_preprocess": ("hbm", 2.0 * B * N * H * d * 2 + 4.0 * B * H * N),   # read O, dO; write D
+        "bwd_preprocess": ("hbm", 2.0 * B * N * H * d * 2 + 12.0 * B * H * N),  # read O, dO, LSE; write D, -LSE log2 e
     }
     dom = max(avg, key=avg.get)
     bound, work = alg[dom]

@@ -43,11 +43,11 @@ def load() -> ctypes.CDLL:
                        ("fa_backward", bwd_args), ("fa_backward_f32", bwd_args)):
         fn = getattr(lib, name)
         fn.argtypes, fn.restype = args, I
-    lib.fa_backward_preprocess.argtypes = [P, P, P, I, I, I, I, P]
+    lib.fa_backward_preprocess.argtypes = [P, P, P, P, I, I, I, I, P]
     lib.fa_backward_preprocess.restype = I
     for name in ("fa_backward_dkdv", "fa_backward_dq"):
         fn = getattr(lib, name)
-        fn.argtypes = [P] * (8 if name == "fa_backward_dkdv" else 7) + [I, I, I, I, F, I, P]
+        fn.argtypes = [P] * (7 if name == "fa_backward_dkdv" else 6) + [I, I, I, I, F, I, P]
         fn.restype = I
     lib.fa_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.fa_backward_workspace_bytes.restype = S
@@ -117,30 +117,38 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float, causal
                    _stream(stream)))
 
 
-def fa_backward_preprocess(o, do, workspace, stream=None):
-    """fa_backward_preprocess: workspace = D = rowsum(dO * O) (bf16 tensors)."""
+def _check_ws(workspace, B, H, N, d):
+    if workspace.numel() * 4 < fa_backward_workspace_bytes(B, H, N, d):
+        raise ValueError("workspace smaller than fa_backward_workspace_bytes()")
+
+
+def fa_backward_preprocess(o, do, lse, workspace, stream=None):
+    """fa_backward_preprocess: workspace = [D = rowsum(dO * O) | -LSE log2(e)] (bf16 tensors)."""
     B, N, H, d = _shape(o)
     _check((o, do), torch.bfloat16)
-    _check((workspace,), torch.float32)
+    _check((lse, workspace), torch.float32)
+    _check_ws(workspace, B, H, N, d)
     _call("fa_backward_preprocess", load().fa_backward_preprocess(
-        _ptr(o), _ptr(do), _ptr(workspace), B, H, N, d, _stream(stream)))
+        _ptr(o), _ptr(do), _ptr(lse), _ptr(workspace), B, H, N, d, _stream(stream)))
 
 
-def fa_backward_dkdv(q, k, v, do, lse, workspace, dk, dv, scale: float, causal: bool, stream=None):
-    """fa_backward_dkdv: dK and dV given D in `workspace` (bf16 tensors)."""
+def fa_backward_dkdv(q, k, v, do, workspace, dk, dv, scale: float, causal: bool, stream=None):
+    """fa_backward_dkdv: dK and dV from the preprocessed workspace (bf16 tensors)."""
     B, N, H, d = _shape(q)
     _check((q, k, v, do, dk, dv), torch.bfloat16)
-    _check((lse, workspace), torch.float32)
+    _check((workspace,), torch.float32)
+    _check_ws(workspace, B, H, N, d)
     _call("fa_backward_dkdv", load().fa_backward_dkdv(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace), _ptr(dk), _ptr(dv),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace), _ptr(dk), _ptr(dv),
         B, H, N, d, float(scale), int(bool(causal)), _stream(stream)))
 
 
-def fa_backward_dq(q, k, v, do, lse, workspace, dq, scale: float, causal: bool, stream=None):
-    """fa_backward_dq: dQ given D in `workspace` (bf16 tensors)."""
+def fa_backward_dq(q, k, v, do, workspace, dq, scale: float, causal: bool, stream=None):
+    """fa_backward_dq: dQ from the preprocessed workspace (bf16 tensors)."""
     B, N, H, d = _shape(q)
     _check((q, k, v, do, dq), torch.bfloat16)
-    _check((lse, workspace), torch.float32)
+    _check((workspace,), torch.float32)
+    _check_ws(workspace, B, H, N, d)
     _call("fa_backward_dq", load().fa_backward_dq(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace), _ptr(dq),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace), _ptr(dq),
         B, H, N, d, float(scale), int(bool(causal)), _stream(stream)))

@@ -79,34 +79,34 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
                                        static_cast<hipStream_t>(stream)));
 }
 
-fa_status fa_backward_preprocess(const void* O, const void* dO, float* workspace,
+fa_status fa_backward_preprocess(const void* O, const void* dO, const float* LSE, float* workspace,
                                  int B, int H, int N, int d, void* stream) {
   fa_status st = check_common(B, H, N, d, 1.f, 0);
-  if (st == FA_OK) st = check_tensors({O, dO}, {workspace});
+  if (st == FA_OK) st = check_tensors({O, dO}, {LSE, workspace});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, 1.f, 0};
-  return to_status(fa::launch_bwd_pre_bf16(O, dO, workspace, s, static_cast<hipStream_t>(stream)));
+  return to_status(fa::launch_bwd_pre_bf16(O, dO, LSE, workspace, s, static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
-                           const float* LSE, const float* workspace, void* dK, void* dV,
+                           const float* workspace, void* dK, void* dV,
                            int B, int H, int N, int d, float scale, int causal, void* stream) {
   fa_status st = check_common(B, H, N, d, scale, causal);
-  if (st == FA_OK) st = check_tensors({Q, K, V, dO, dK, dV}, {LSE, workspace});
+  if (st == FA_OK) st = check_tensors({Q, K, V, dO, dK, dV}, {workspace});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, scale, causal};
-  return to_status(fa::launch_bwd_dkdv_bf16(Q, K, V, dO, LSE, workspace, dK, dV, s,
+  return to_status(fa::launch_bwd_dkdv_bf16(Q, K, V, dO, workspace, dK, dV, s,
                                             static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_backward_dq(const void* Q, const void* K, const void* V, const void* dO,
-                         const float* LSE, const float* workspace, void* dQ,
+                         const float* workspace, void* dQ,
                          int B, int H, int N, int d, float scale, int causal, void* stream) {
   fa_status st = check_common(B, H, N, d, scale, causal);
-  if (st == FA_OK) st = check_tensors({Q, K, V, dO, dQ}, {LSE, workspace});
+  if (st == FA_OK) st = check_tensors({Q, K, V, dO, dQ}, {workspace});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, scale, causal};
-  return to_status(fa::launch_bwd_dq_bf16(Q, K, V, dO, LSE, workspace, dQ, s,
+  return to_status(fa::launch_bwd_dq_bf16(Q, K, V, dO, workspace, dQ, s,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -124,7 +124,7 @@ fa_status fa_backward_f32(const float* Q, const float* K, const float* V, const 
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   if (check_common(B, H, N, d, 1.f, 0) != FA_OK) return 0;
-  return (size_t)B * H * N * sizeof(float);
+  return 2 * (size_t)B * H * N * sizeof(float);
 }
 
 const char* fa_status_string(int status) {

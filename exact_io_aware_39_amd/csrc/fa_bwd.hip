@@ -11,18 +11,23 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three launches on one stream, no atomics (results are bit-reproducible):
-//   1. bwd_pre  : D = rowsum(dO * O) in fp32, streaming both tensors once.
+//   1. bwd_pre  : workspace = [D | -LSE log2(e)], streaming O and dO once, so
+//                 that P = exp2(c S + nl) is one FMA and one exp per element.
 //   2. bwd_dkdv : one workgroup per 128 keys (32 per wave, K and V of those
 //                 keys resident in registers); walks the query tiles that can
-//                 see them, staging Q, dO, LSE and D through double-buffered
-//                 LDS.  S = Q K^T and dP = dO V^T use 32x32x16 MFMA with the
-//                 key as the lane, so P and dS come out in the B-operand
-//                 layout of dV^T += dO^T P and dK^T += Q^T dS, whose A
-//                 operands are transposing LDS reads of the dO and Q tiles.
+//                 see them.  S = Q K^T and dP = dO V^T use 32x32x16 MFMA with
+//                 the key as the lane, so P and dS come out in the B-operand
+//                 layout of dV^T += dO^T P and dK^T += Q^T dS, whose A operands
+//                 are transposing LDS reads of the dO and Q tiles.
 //   3. bwd_dq   : one workgroup per 128 queries (32 per wave, Q and dO of those
 //                 rows resident); walks the key tiles they can see.  S^T and
-//                 dP^T have the query as the lane, so LSE_i and D_i are one
-//                 scalar per lane, and dS^T feeds dQ^T += K^T dS^T directly.
+//                 dP^T have the query as the lane, so the row statistics are
+//                 one scalar per lane, and dS^T feeds dQ^T += K^T dS^T directly.
+// Both passes stage their streamed tiles with buffer -> LDS copies into a ring
+// of LDS slots and, at head size 64, software-pipeline the two score-like
+// products of the next tile ahead of the exp / dS work of the current one.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -36,24 +41,25 @@ struct BwdArgs {
   const __bf16* o;
   const __bf16* dout;
   const float* lse;
-  const float* dvec;
+  float* ws;          // [D (B*H*N) | -LSE*log2(e) (B*H*N)]
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* dvec_out;
   int H, N, ntiles;
-  float c;       // scale * log2(e)
+  int64_t bhn;        // B*H*N
+  float c;            // scale * log2(e)
   float scale;
 };
 
-// ------------------------------------------------------------------ D = rowsum(dO * O)
+// ------------------------------------------------------------------ preprocess
 // CH = D/8 lanes share a row, each reading one 16-byte chunk of O and of dO;
 // the whole [B, N, H, d] tensors are read front to back.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ o,
                                                       const __bf16* __restrict__ dout,
-                                                      float* __restrict__ dvec, int H, int N,
-                                                      int64_t rows) {
+                                                      const float* __restrict__ lse,
+                                                      float* __restrict__ ws, int H, int N,
+                                                      int64_t rows, int64_t bhn) {
   constexpr int CH = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t r = gid / CH;
@@ -70,26 +76,57 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   if (r < rows && ch == 0) {
     const int64_t h = r % H, bn = r / H;
     const int64_t n = bn % N, b = bn / N;
-    dvec[(b * H + h) * N + n] = acc;
+    const int64_t idx = (b * H + h) * N + n;
+    ws[idx] = acc;
+    ws[bhn + idx] = -lse[idx] * kLog2e;
   }
 }
 
-// A-operand fragment of a transposed tile: element (row = d, k = tile row) of
-// the 32x32x16 MFMA for output d-tile t and k-step u of a 32-row block j.
-// Lane l gets d = 32 t + l%32 and tile rows 32 j + 16 u + 4 (l/32) + {0..3}
-// (low half) and the same + 8 (high half), matching the B operand built from
-// accumulator registers 8u .. 8u+7 of a C fragment.
+// Lane base for the A operand of a row-major tile read 16 bytes per lane:
+// row l%32 (+ 32 j), logical chunk 2 ks + l/32; address = base ^ (ks << 5).
 template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int lane, int t, int j, int u) {
-  const int i = lane & 15, g = lane >> 4;
-  const int row = 32 * j + 16 * u + (g >> 1) * 4 + (i >> 2);
-  const int col = t * 32 + (g & 1) * 16 + (i & 3) * 4;
-  const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_read_tr16(tile, elem_off<D>(row, col)));
-  const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_read_tr16(tile, elem_off<D>(row + 8, col)));
+__device__ __forceinline__ uint32_t row_frag_base(int lane) {
+  const int hh = lane >> 5, l32 = lane & 31;
+  return (uint32_t)(l32 * D * 2) | ((uint32_t)(hh ^ swz<D>(l32)) << 4);
+}
+
+// Lane base for the transposing read (A operand = tile^T): within each group of
+// 16 lanes, lane i addresses row 4 (l/32) + i/4 and element column
+// 16 ((l/16)%2) + 4 (i%4); address = base ^ (64 t [+ 32 for rows + 8]).
+template <int D>
+__device__ __forceinline__ uint32_t tr_frag_base(int lane) {
+  const int ti = lane & 15, tg = lane >> 4;
+  const int r4 = (tg >> 1) * 4 + (ti >> 2);
+  const int cl = (tg & 1) * 2 + ((ti & 3) >> 1);
+  return (uint32_t)(r4 * D * 2) | ((uint32_t)(cl ^ swz<D>(r4)) << 4) | ((uint32_t)(ti & 1) << 3);
+}
+
+// A fragment of tile^T: rows d = 32 t + l%32, tile rows 32 j + 16 u + 4 (l/32)
+// + {0..3} and the same + 8, matching the B operand built from accumulator
+// registers 8u .. 8u+7 of a C fragment of rows 32 j .. 32 j + 31.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, uint32_t base, int t, int j, int u) {
+  const uint32_t rowoff = (uint32_t)((32 * j + 16 * u) * D * 2);
+  const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_read_tr16(tile, (base ^ (64 * t)) + rowoff));
+  const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_read_tr16(tile, (base ^ (64 * t + 32)) + rowoff + 8 * D * 2));
   bf16x8 r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
   r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   return r;
+}
+
+// Per-lane byte offsets of the buffer -> LDS copies of a tile of ROWS rows:
+// copy i of a wave fills LDS block (wave + 4 i); lane l holds physical chunk
+// slot%CH of row slot/CH, i.e. logical chunk (slot%CH) ^ swz(row).
+template <int D, int CPW>
+__device__ __forceinline__ void stage_offsets(uint32_t (&voff)[CPW], int wave, int lane, int64_t rs) {
+  constexpr int CH = D / 8;
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int slot = (wave + 4 * i) * 64 + lane;
+    const int row = slot / CH;
+    voff[i] = (uint32_t)(row * rs * 2) + (uint32_t)(((slot % CH) ^ swz<D>(row)) * 16);
+  }
 }
 
 // Write a C fragment holding rows d of one key/query column (this lane's row
@@ -113,12 +150,13 @@ constexpr int kBq = 32;           // queries per step
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int CH = D / 8, KS = D / 16, DT = D / 32;
-  constexpr int TILE = kBq * D * 2;
-  constexpr int CPT = (kBq * CH + 255) / 256;   // chunks per thread per tensor
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];   // [stage][Q, dO]
-  __shared__ __attribute__((aligned(16))) float sl[2][kBq];        // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float sd[2][kBq];        // D
+  constexpr bool PIPE = D == 64;            // score products of the next tile run ahead
+  constexpr int NSLOT = PIPE ? 3 : 2;
+  constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
+  constexpr int TILE = kBq * RB;            // one Q or dO tile
+  constexpr int CPW = TILE / 1024 / 4;      // 1 KB copies per wave per tile
+  constexpr int SLOT = 2 * TILE + 512;      // Q, dO, then 64 floats of -LSE log2 e and of D
+  __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -129,8 +167,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
   const int N = a.N;
   const int64_t rs = (int64_t)a.H * D;
   const int64_t base = ((int64_t)b * N * a.H + h) * D;
-  const float* lse = a.lse + (int64_t)bh * N;
-  const float* dvec = a.dvec + (int64_t)bh * N;
+  const float* dstat = a.ws + (int64_t)bh * N;
+  const float* nlstat = a.ws + a.bhn + (int64_t)bh * N;
 
   const int k0 = kt * kKeysPerWg;
   const int kw0 = k0 + 32 * wave;
@@ -153,101 +191,117 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
   const int qstart = CAUSAL ? k0 : 0;
   const int nsteps = (N - qstart + kBq - 1) / kBq;
 
-  u32x4 qreg[CPT], greg[CPT];
-  float lreg = 0.f, dreg = 0.f;
-  auto gload = [&](int s) {
+  uint32_t voff[CPW];
+  stage_offsets<D, CPW>(voff, wave, lane, rs);
+  // Copies of query tile s (rows past N and statistics past N read as zero).
+  auto stage = [&](int s, char* slot) {
     const int qi0 = qstart + s * kBq;
+    const int rows = min(N - qi0, kBq);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + base + (int64_t)qi0 * rs, (uint32_t)(rows * rs * 2));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.dout + base + (int64_t)qi0 * rs, (uint32_t)(rows * rs * 2));
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < kBq * CH) {
-        const int row = idx / CH, ch = idx % CH;
-        const int64_t qr = min(qi0 + row, N - 1);
-        qreg[i] = *reinterpret_cast<const u32x4*>(a.q + base + qr * rs + ch * 8);
-        greg[i] = *reinterpret_cast<const u32x4*>(a.dout + base + qr * rs + ch * 8);
-      }
+    for (int i = 0; i < CPW; ++i) {
+      buffer_to_lds16(rq, voff[i], slot + (wave + 4 * i) * 1024);
+      buffer_to_lds16(rg, voff[i], slot + TILE + (wave + 4 * i) * 1024);
     }
-    if (tid < kBq) {
-      const int qr = min(qi0 + tid, N - 1);
-      lreg = lse[qr] * kLog2e;
-      dreg = dvec[qr];
-    }
-  };
-  auto swrite = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < kBq * CH) {
-        const int row = idx / CH, ch = idx % CH;
-        const uint32_t off = tile_off<D>(row, ch);
-        *reinterpret_cast<u32x4*>(smem[stage][0] + off) = qreg[i];
-        *reinterpret_cast<u32x4*>(smem[stage][1] + off) = greg[i];
-      }
-    }
-    if (tid < kBq) {
-      sl[stage][tid] = lreg;
-      sd[stage][tid] = dreg;
-    }
+    if (wave == 0)
+      buffer_to_lds4(make_rsrc(nlstat + qi0, (uint32_t)(rows * 4)), lane * 4, slot + 2 * TILE);
+    else if (wave == 1)
+      buffer_to_lds4(make_rsrc(dstat + qi0, (uint32_t)(rows * 4)), lane * 4, slot + 2 * TILE + 256);
   };
 
-  const float c = a.c;
-  gload(0);
-  for (int s = 0; s < nsteps; ++s) {
-    const int stage = s & 1;
-    swrite(stage);
-    __syncthreads();
-    if (s + 1 < nsteps) gload(s + 1);
-
-    const int qi0 = qstart + s * kBq;
-    if (CAUSAL && qi0 + kBq - 1 < kw0) continue;   // every query precedes this wave's keys
-    const char* qt = smem[stage][0];
-    const char* gt = smem[stage][1];
-
-    // S = Q K^T and dP = dO V^T: lane = key, register r = query row 8(r/4) + 4hh + r%4.
-    f32x16 sacc = (f32x16){}, pacc = (f32x16){};
+  const uint32_t rfb = row_frag_base<D>(lane);
+  const uint32_t tfb = tr_frag_base<D>(lane);
+  // S = Q K^T and dP = dO V^T: lane = key, register r = query row 8(r/4) + 4hh + r%4.
+  auto scores = [&](const char* slot, f32x16& sacc, f32x16& pacc) {
+    sacc = (f32x16){};
+    pacc = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 qa = lds_read_b128(qt, tile_off<D>(l32, 2 * ks + hh));
-      const bf16x8 ga = lds_read_b128(gt, tile_off<D>(l32, 2 * ks + hh));
-      sacc = mfma32x32x16(qa, kf[ks], sacc);
-      pacc = mfma32x32x16(ga, vf[ks], pacc);
+      sacc = mfma32x32x16(lds_read_b128(slot, rfb ^ (ks << 5)), kf[ks], sacc);
+      pacc = mfma32x32x16(lds_read_b128(slot + TILE, rfb ^ (ks << 5)), vf[ks], pacc);
     }
-    f32x4 lq[4], dq4[4];
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      lq[g4] = *reinterpret_cast<const f32x4*>(&sl[stage][8 * g4 + 4 * hh]);
-      dq4[g4] = *reinterpret_cast<const f32x4*>(&sd[stage][8 * g4 + 4 * hh]);
-    }
-    const bool masked = (qi0 + kBq > N) || (CAUSAL && kw0 + 31 > qi0);
-    float p[16], ds[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float lv = lq[r >> 2][r & 3], dv4 = dq4[r >> 2][r & 3];
-      float pv = fast_exp2(__builtin_fmaf(sacc[r], c, -lv));
-      if (masked) {
-        const int qrow = qi0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool hide = qrow >= N || (CAUSAL && mykey > qrow);
-        pv = hide ? 0.f : pv;
-      }
-      p[r] = pv;
-      ds[r] = pv * (pacc[r] - dv4);
-    }
-    bf16x8 pb[2], db[2];
+  };
+  const float c = a.c;
+  // P, dS for one query tile and the dV, dK updates.
+  auto update = [&](auto mask_tag, const char* slot, const f32x16& sacc, const f32x16& pacc, int qi0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // Query rows 16 u .. 16 u + 15 of the tile (registers 8u .. 8u+7) at a time.
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      pb[u] = pack_bf16x8(p[8 * u], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3],
-                          p[8 * u + 4], p[8 * u + 5], p[8 * u + 6], p[8 * u + 7]);
-      db[u] = pack_bf16x8(ds[8 * u], ds[8 * u + 1], ds[8 * u + 2], ds[8 * u + 3],
-                          ds[8 * u + 4], ds[8 * u + 5], ds[8 * u + 6], ds[8 * u + 7]);
-    }
-    // dV^T += dO^T P ; dK^T += Q^T dS   (rows d, columns keys)
+      float p[8], ds[8];
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+      for (int g = 0; g < 2; ++g) {
+        const int g4 = 2 * u + g;
+        const f32x4 nl = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + (8 * g4 + 4 * hh) * 4);
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (8 * g4 + 4 * hh) * 4);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        dv[t] = mfma32x32x16(tr_frag<D>(gt, lane, t, 0, u), pb[u], dv[t]);
-        dk[t] = mfma32x32x16(tr_frag<D>(qt, lane, t, 0, u), db[u], dk[t]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float pv = fast_exp2(__builtin_fmaf(sacc[r], c, nl[e]));
+          if constexpr (MASK) {
+            const int qrow = qi0 + 8 * g4 + 4 * hh + e;
+            const bool hide = qrow >= N || (CAUSAL && mykey > qrow);
+            pv = hide ? 0.f : pv;
+          }
+          p[4 * g + e] = pv;
+          ds[4 * g + e] = pv * (pacc[r] - dd[e]);
+        }
       }
+      const bf16x8 pb = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      const bf16x8 db = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+      // dV^T += dO^T P ; dK^T += Q^T dS   (rows d, columns keys)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        dv[t] = mfma32x32x16(tr_frag<D>(slot + TILE, tfb, t, 0, u), pb, dv[t]);
+        dk[t] = mfma32x32x16(tr_frag<D>(slot, tfb, t, 0, u), db, dk[t]);
+      }
+    }
+  };
+  auto update_tile = [&](const char* slot, const f32x16& sacc, const f32x16& pacc, int s) {
+    const int qi0 = qstart + s * kBq;
+    if (CAUSAL && qi0 + kBq - 1 < kw0) return;   // every query precedes this wave's keys
+    const bool masked = (qi0 + kBq > N) || (CAUSAL && kw0 + 31 > qi0);
+    if (__builtin_expect(masked, 0)) update(std::true_type{}, slot, sacc, pacc, qi0);
+    else update(std::false_type{}, slot, sacc, pacc, qi0);
+  };
+
+  if constexpr (PIPE) {
+    // Step s: copies of tile s+2, score products of tile s+1 (a stale slot on
+    // the last step; the result is unused), then P, dS and dV, dK of tile s.
+    auto slot_of = [&](int s) { return smem + (s % NSLOT) * SLOT; };
+    auto step = [&](int s, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn) {
+      wait_vmem();
+      __syncthreads();
+      if (s + 2 < nsteps) stage(s + 2, slot_of(s + 2));
+      scores(slot_of(s + 1), sn, pn);
+      update_tile(slot_of(s), sc, pc, s);
+    };
+    stage(0, slot_of(0));
+    if (nsteps > 1) stage(1, slot_of(1));
+    wait_vmem();
+    __syncthreads();
+    f32x16 sa, pa, sb, pb2;
+    scores(slot_of(0), sa, pa);
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+      step(s, sa, pa, sb, pb2);
+      step(s + 1, sb, pb2, sa, pa);
+    }
+    if (s < nsteps) step(s, sa, pa, sb, pb2);
+  } else {
+    stage(0, smem);
+    for (int s = 0; s < nsteps; ++s) {
+      char* slot = smem + (s & 1) * SLOT;
+      wait_vmem();
+      __syncthreads();
+      if (s + 1 < nsteps) stage(s + 1, smem + ((s + 1) & 1) * SLOT);
+      const int qi0 = qstart + s * kBq;
+      if (CAUSAL && qi0 + kBq - 1 < kw0) continue;
+      f32x16 sacc, pacc;
+      scores(slot, sacc, pacc);
+      update_tile(slot, sacc, pacc, s);
+    }
   }
 
   if (mykey < N) {
@@ -262,10 +316,15 @@ constexpr int kBk = 64;        // keys per step
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int CH = D / 8, KS = D / 16, DT = D / 32;
-  constexpr int TILE = kBk * D * 2;
-  constexpr int CPT = kBk * CH / 256;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];   // [stage][K, V]
+  // Three K and three V slots: step t reads tiles t and t+1 while tile t+2 is
+  // being copied.
+  constexpr int NS = 3;
+  constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
+  constexpr int TILE = kBk * RB;
+  constexpr int CPW = TILE / 1024 / 4;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];   // K slots, then V slots
+  char* const kbuf = smem;
+  char* const vbuf = smem + NS * TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -288,8 +347,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + base + (int64_t)qc * rs + (2 * ks + hh) * 8);
     gf[ks] = *reinterpret_cast<const bf16x8*>(a.dout + base + (int64_t)qc * rs + (2 * ks + hh) * 8);
   }
-  const float lse2 = a.lse[(int64_t)bh * N + qc] * kLog2e;
-  const float dval = a.dvec[(int64_t)bh * N + qc];
+  const float nl2 = a.ws[a.bhn + (int64_t)bh * N + qc];
+  const float dval = a.ws[(int64_t)bh * N + qc];
 
   f32x16 dq[DT];
 #pragma unroll
@@ -297,79 +356,92 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int kend = CAUSAL ? min(N, q0 + kQPerWg) : N;
   const int nkt = (kend + kBk - 1) / kBk;
-  u32x4 kreg[CPT], vreg[CPT];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / CH, ch = idx % CH;
-      const int64_t key = min(kt * kBk + row, N - 1);
-      kreg[i] = *reinterpret_cast<const u32x4*>(a.k + base + key * rs + ch * 8);
-      vreg[i] = *reinterpret_cast<const u32x4*>(a.v + base + key * rs + ch * 8);
-    }
-  };
-  auto swrite = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / CH, ch = idx % CH;
-      const uint32_t off = tile_off<D>(row, ch);
-      *reinterpret_cast<u32x4*>(smem[stage][0] + off) = kreg[i];
-      *reinterpret_cast<u32x4*>(smem[stage][1] + off) = vreg[i];
-    }
-  };
 
+  uint32_t voff[CPW];
+  stage_offsets<D, CPW>(voff, wave, lane, rs);
+  auto stage_rows = [&](const __bf16* src, int t, char* dst) {
+    const int rows = min(N - t * kBk, kBk);
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src + base + (int64_t)t * kBk * rs, (uint32_t)(rows * rs * 2));
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, voff[i], dst + (wave + 4 * i) * 1024);
+  };
+  auto kslot = [&](int t) { return kbuf + (t % NS) * TILE; };
+  auto vslot = [&](int t) { return vbuf + (t % NS) * TILE; };
+
+  const uint32_t rfb = row_frag_base<D>(lane);
+  const uint32_t tfb = tr_frag_base<D>(lane);
+  // S^T = K Q^T and dP^T = V dO^T for 32-key sub-tile j of a K/V slot pair:
+  // lane = query, register r = key 32 j + 8(r/4) + 4hh + r%4.
+  auto scores = [&](const char* kt, const char* vt, int j, f32x16& sacc, f32x16& pacc) {
+    sacc = (f32x16){};
+    pacc = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      sacc = mfma32x32x16(lds_read_b128(kt, (rfb ^ (ks << 5)) + 32 * j * RB), qf[ks], sacc);
+      pacc = mfma32x32x16(lds_read_b128(vt, (rfb ^ (ks << 5)) + 32 * j * RB), gf[ks], pacc);
+    }
+  };
   const float c = a.c;
-  gload(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int stage = kt & 1;
-    swrite(stage);
-    __syncthreads();
-    if (kt + 1 < nkt) gload(kt + 1);
-
-    const int k0 = kt * kBk;
-    if (CAUSAL && k0 > qw0 + 31) continue;
-    const char* ktile = smem[stage][0];
-    const char* vtile = smem[stage][1];
-    const bool masked = (k0 + kBk > N) || (CAUSAL && k0 + kBk - 1 > qw0);
-
-    bf16x8 db[2][2];
+  auto update = [&](auto mask_tag, const char* kt, int j, const f32x16& sacc, const f32x16& pacc, int k0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // S^T = K Q^T and dP^T = V dO^T: lane = query, register r = key 8(r/4) + 4hh + r%4.
-      f32x16 sacc = (f32x16){}, pacc = (f32x16){};
+    for (int u = 0; u < 2; ++u) {
+      float ds[8];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = lds_read_b128(ktile, tile_off<D>(32 * j + l32, 2 * ks + hh));
-        const bf16x8 va = lds_read_b128(vtile, tile_off<D>(32 * j + l32, 2 * ks + hh));
-        sacc = mfma32x32x16(ka, qf[ks], sacc);
-        pacc = mfma32x32x16(va, gf[ks], pacc);
-      }
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(__builtin_fmaf(sacc[r], c, -lse2));
-        if (masked) {
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * u + e;
+        float pv = fast_exp2(__builtin_fmaf(sacc[r], c, nl2));
+        if constexpr (MASK) {
           const int key = k0 + 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
           const bool hide = key >= N || (CAUSAL && key > myq);
           pv = hide ? 0.f : pv;
         }
-        ds[r] = pv * (pacc[r] - dval);
+        ds[e] = pv * (pacc[r] - dval);
       }
+      const bf16x8 db = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+      // dQ^T += K^T dS^T (rows d, columns queries)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        db[j][u] = pack_bf16x8(ds[8 * u], ds[8 * u + 1], ds[8 * u + 2], ds[8 * u + 3],
-                               ds[8 * u + 4], ds[8 * u + 5], ds[8 * u + 6], ds[8 * u + 7]);
+      for (int t = 0; t < DT; ++t) dq[t] = mfma32x32x16(tr_frag<D>(kt, tfb, t, j, u), db, dq[t]);
     }
-    // dQ^T += K^T dS^T (rows d, columns queries)
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          dq[t] = mfma32x32x16(tr_frag<D>(ktile, lane, t, j, u), db[j][u], dq[t]);
+  };
+  // dS and dQ for sub-tile j of key tile t.
+  auto update_sub = [&](int t, int j, const f32x16& sacc, const f32x16& pacc) {
+    const int k0 = t * kBk;
+    if (CAUSAL && k0 + 32 * j > qw0 + 31) return;   // these keys lie past the wave's rows
+    const bool masked = (k0 + 32 * j + 32 > N) || (CAUSAL && k0 + 32 * j + 31 > qw0);
+    if (__builtin_expect(masked, 0)) update(std::true_type{}, kslot(t), j, sacc, pacc, k0);
+    else update(std::false_type{}, kslot(t), j, sacc, pacc, k0);
+  };
+
+  // Software pipeline over 32-key units: the score products of the next unit
+  // (the other half of this tile, or the first half of tile t+1, which was
+  // copied one step ahead) are issued before the dS work of the current unit.
+  // Step t: copies of tile t+2, then units (t, 0) and (t, 1).  On the last
+  // step the look-ahead reads a stale slot and its result is unused.
+  auto step = [&](int t, f32x16& sa, f32x16& pa, f32x16& sb, f32x16& pb2) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 2 < nkt) {
+      stage_rows(a.k, t + 2, kslot(t + 2));
+      stage_rows(a.v, t + 2, vslot(t + 2));
+    }
+    if (CAUSAL && t * kBk > qw0 + 31) return;   // this and later tiles lie past the wave's rows
+    scores(kslot(t), vslot(t), 1, sb, pb2);
+    update_sub(t, 0, sa, pa);
+    scores(kslot(t + 1), vslot(t + 1), 0, sa, pa);
+    update_sub(t, 1, sb, pb2);
+  };
+  stage_rows(a.k, 0, kslot(0));
+  stage_rows(a.v, 0, vslot(0));
+  if (nkt > 1) {
+    stage_rows(a.k, 1, kslot(1));
+    stage_rows(a.v, 1, vslot(1));
   }
+  wait_vmem();
+  __syncthreads();
+  f32x16 sa, pa, sb, pb2;
+  scores(kslot(0), vslot(0), 0, sa, pa);
+  for (int t = 0; t < nkt; ++t) step(t, sa, pa, sb, pb2);
 
   if (myq < N) store_row_frags<D>(a.dq + base + (int64_t)myq * rs, dq, hh, a.scale);
 }
@@ -379,7 +451,7 @@ hipError_t run_pre(const BwdArgs& a, int B, hipStream_t st) {
   const int64_t rows = (int64_t)B * a.N * a.H;
   const int64_t threads = rows * (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                     a.o, a.dout, a.dvec_out, a.H, a.N, rows);
+                     a.o, a.dout, a.lse, a.ws, a.H, a.N, rows, a.bhn);
   return hipGetLastError();
 }
 
@@ -402,8 +474,7 @@ hipError_t run_dq(BwdArgs a, int BH, bool causal, hipStream_t st) {
 }
 
 BwdArgs make_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                  const float* lse, const float* dvec_in, float* dvec_out, void* dq, void* dk,
-                  void* dv, const AttnShape& s) {
+                  const float* lse, float* ws, void* dq, void* dk, void* dv, const AttnShape& s) {
   BwdArgs a{};
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
@@ -411,13 +482,13 @@ BwdArgs make_args(const void* q, const void* k, const void* v, const void* o, co
   a.o = static_cast<const __bf16*>(o);
   a.dout = static_cast<const __bf16*>(dout);
   a.lse = lse;
-  a.dvec = dvec_in;
-  a.dvec_out = dvec_out;
+  a.ws = ws;
   a.dq = static_cast<__bf16*>(dq);
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
   a.H = s.H;
   a.N = s.N;
+  a.bhn = (int64_t)s.B * s.H * s.N;
   a.c = s.scale * kLog2e;
   a.scale = s.scale;
   return a;
@@ -425,26 +496,24 @@ BwdArgs make_args(const void* q, const void* k, const void* v, const void* o, co
 
 }  // namespace
 
-hipError_t launch_bwd_pre_bf16(const void* o, const void* dout, float* dvec, const AttnShape& s,
-                               hipStream_t stream) {
-  const BwdArgs a = make_args(nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, dvec, nullptr,
-                              nullptr, nullptr, s);
+hipError_t launch_bwd_pre_bf16(const void* o, const void* dout, const float* lse, float* ws,
+                               const AttnShape& s, hipStream_t stream) {
+  const BwdArgs a = make_args(nullptr, nullptr, nullptr, o, dout, lse, ws, nullptr, nullptr, nullptr, s);
   return s.d == 64 ? run_pre<64>(a, s.B, stream) : run_pre<128>(a, s.B, stream);
 }
 
 hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout,
-                                const float* lse, const float* dvec, void* dk, void* dv,
-                                const AttnShape& s, hipStream_t stream) {
-  const BwdArgs a = make_args(q, k, v, nullptr, dout, lse, dvec, nullptr, nullptr, dk, dv, s);
+                                const float* ws, void* dk, void* dv, const AttnShape& s,
+                                hipStream_t stream) {
+  const BwdArgs a = make_args(q, k, v, nullptr, dout, nullptr, const_cast<float*>(ws), nullptr, dk, dv, s);
   const int BH = s.B * s.H;
   return s.d == 64 ? run_dkdv<64>(a, BH, s.causal != 0, stream)
                    : run_dkdv<128>(a, BH, s.causal != 0, stream);
 }
 
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout,
-                              const float* lse, const float* dvec, void* dq, const AttnShape& s,
-                              hipStream_t stream) {
-  const BwdArgs a = make_args(q, k, v, nullptr, dout, lse, dvec, nullptr, dq, nullptr, nullptr, s);
+                              const float* ws, void* dq, const AttnShape& s, hipStream_t stream) {
+  const BwdArgs a = make_args(q, k, v, nullptr, dout, nullptr, const_cast<float*>(ws), dq, nullptr, nullptr, s);
   const int BH = s.B * s.H;
   return s.d == 64 ? run_dq<64>(a, BH, s.causal != 0, stream)
                    : run_dq<128>(a, BH, s.causal != 0, stream);
@@ -452,10 +521,10 @@ hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           float* dvec, const AttnShape& s, hipStream_t stream) {
-  hipError_t e = launch_bwd_pre_bf16(o, dout, dvec, s, stream);
-  if (e == hipSuccess) e = launch_bwd_dkdv_bf16(q, k, v, dout, lse, dvec, dk, dv, s, stream);
-  if (e == hipSuccess) e = launch_bwd_dq_bf16(q, k, v, dout, lse, dvec, dq, s, stream);
+                           float* ws, const AttnShape& s, hipStream_t stream) {
+  hipError_t e = launch_bwd_pre_bf16(o, dout, lse, ws, s, stream);
+  if (e == hipSuccess) e = launch_bwd_dkdv_bf16(q, k, v, dout, ws, dk, dv, s, stream);
+  if (e == hipSuccess) e = launch_bwd_dq_bf16(q, k, v, dout, ws, dq, s, stream);
   return e;
 }
 

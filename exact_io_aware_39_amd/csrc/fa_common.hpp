@@ -131,6 +131,11 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds_block, 16, voff, 0, 0, 0);
 }
 
+// Asynchronous 4-byte buffer -> LDS copy: lane l's dword lands at lds_block + 4 l.
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds_block, 4, voff, 0, 0, 0);
+}
+
 // Wait until this wave's global loads (including global -> LDS copies) are done.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

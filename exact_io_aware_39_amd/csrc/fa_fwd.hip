@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     scores(kbuf + ((kt + 1) & 1) * TILE, snext);
     const char* vb = vbuf + (kt & 1) * TILE;
     const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
-    if (masked) softmax_pv(std::true_type{}, scur, vb, k0);
+    if (__builtin_expect(masked, 0)) softmax_pv(std::true_type{}, scur, vb, k0);
     else softmax_pv(std::false_type{}, scur, vb, k0);
   };
 

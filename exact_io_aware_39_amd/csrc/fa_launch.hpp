@@ -21,14 +21,13 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
                            float* dvec, const AttnShape& s, hipStream_t stream);
-hipError_t launch_bwd_pre_bf16(const void* o, const void* dout, float* dvec, const AttnShape& s,
-                               hipStream_t stream);
+hipError_t launch_bwd_pre_bf16(const void* o, const void* dout, const float* lse, float* ws,
+                               const AttnShape& s, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout,
-                                const float* lse, const float* dvec, void* dk, void* dv,
-                                const AttnShape& s, hipStream_t stream);
+                                const float* ws, void* dk, void* dv, const AttnShape& s,
+                                hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout,
-                              const float* lse, const float* dvec, void* dq, const AttnShape& s,
-                              hipStream_t stream);
+                              const float* ws, void* dq, const AttnShape& s, hipStream_t stream);
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                           const float* dout, const float* lse, float* dq, float* dk, float* dv,
                           float* dvec, const AttnShape& s, hipStream_t stream);

@@ -89,7 +89,7 @@ fa_status fa_forward_f32(const float* Q, const float* K, const float* V, float* 
  * of softmax: dV = P^T dO, dP = dO V^T, D_i = rowsum(dO * O)_i,
  * dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
  * `workspace` is caller-owned device memory of fa_backward_workspace_bytes()
- * bytes; on return it holds D ([B, H, N] fp32).
+ * bytes; on return its first B*H*N floats hold D ([B, H, N] fp32).
  */
 fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                       const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
@@ -98,20 +98,22 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
 /*
  * The three passes fa_backward runs, in this order, for callers that schedule
  * them themselves (bf16 tensors, same layouts and checks as fa_backward):
- *   fa_backward_preprocess  workspace[b, h, i] = D_i = sum_c dO_ic O_ic (fp32);
- *   fa_backward_dkdv        dK = scale dS^T Q and dV = P^T dO, reading D from
- *                           `workspace` (written by the preprocess);
- *   fa_backward_dq          dQ = scale dS K, reading D from `workspace`.
- * The dK/dV and dQ passes only read shared inputs, so once the preprocess has
- * completed they may run concurrently on different streams.
+ *   fa_backward_preprocess  fills `workspace` with D_i = sum_c dO_ic O_ic and
+ *                           -LSE_i log2(e) (two fp32 [B, H, N] arrays, in that
+ *                           order);
+ *   fa_backward_dkdv        dK = scale dS^T Q and dV = P^T dO;
+ *   fa_backward_dq          dQ = scale dS K;
+ * the last two read the workspace written by the preprocess.  They only read
+ * shared inputs, so once the preprocess has completed they may run
+ * concurrently on different streams.
  */
-fa_status fa_backward_preprocess(const void* O, const void* dO, float* workspace,
+fa_status fa_backward_preprocess(const void* O, const void* dO, const float* LSE, float* workspace,
                                  int B, int H, int N, int d, void* stream);
 fa_status fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
-                           const float* LSE, const float* workspace, void* dK, void* dV,
+                           const float* workspace, void* dK, void* dV,
                            int B, int H, int N, int d, float scale, int causal, void* stream);
 fa_status fa_backward_dq(const void* Q, const void* K, const void* V, const void* dO,
-                         const float* LSE, const float* workspace, void* dQ,
+                         const float* workspace, void* dQ,
                          int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /* Backward, float32 tensors: same contract as fa_backward, every tensor fp32. */
@@ -120,7 +122,7 @@ fa_status fa_backward_f32(const float* Q, const float* K, const float* V, const 
                           float* workspace, int B, int H, int N, int d, float scale, int causal,
                           void* stream);
 
-/* Bytes of workspace fa_backward / fa_backward_f32 need (0 for invalid sizes). */
+/* Bytes of workspace fa_backward / fa_backward_f32 need: 8 B H N (0 for invalid sizes). */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 
 /* Static, NUL-terminated description of a status code. */

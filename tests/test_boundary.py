@@ -36,11 +36,11 @@ def lib():
     for name in ("fa_backward", "fa_backward_f32"):
         getattr(lib, name).argtypes = [vp] * 10 + [i] * 4 + [f, i, vp]
         getattr(lib, name).restype = i
-    lib.fa_backward_preprocess.argtypes = [vp] * 3 + [i] * 4 + [vp]
+    lib.fa_backward_preprocess.argtypes = [vp] * 4 + [i] * 4 + [vp]
     lib.fa_backward_preprocess.restype = i
-    lib.fa_backward_dkdv.argtypes = [vp] * 8 + [i] * 4 + [f, i, vp]
+    lib.fa_backward_dkdv.argtypes = [vp] * 7 + [i] * 4 + [f, i, vp]
     lib.fa_backward_dkdv.restype = i
-    lib.fa_backward_dq.argtypes = [vp] * 7 + [i] * 4 + [f, i, vp]
+    lib.fa_backward_dq.argtypes = [vp] * 6 + [i] * 4 + [f, i, vp]
     lib.fa_backward_dq.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i] * 4
     lib.fa_backward_workspace_bytes.restype = ctypes.c_size_t
@@ -115,15 +115,17 @@ def test_backward_rejects_bad_arguments(lib, name):
 
 
 def test_backward_passes_reject_bad_arguments(lib):
-    assert lib.fa_backward_preprocess(P, P, P, 1, 1, 128, 96, None) == UNSUPPORTED
-    assert lib.fa_backward_preprocess(P, P, P, 1, 0, 128, 64, None) == INVALID
-    for i in range(3):
-        ptrs = [P] * 3
+    assert lib.fa_backward_preprocess(P, P, P, P, 1, 1, 128, 96, None) == UNSUPPORTED
+    assert lib.fa_backward_preprocess(P, P, P, P, 1, 0, 128, 64, None) == INVALID
+    for i in range(4):
+        ptrs = [P] * 4
         ptrs[i] = None
         assert lib.fa_backward_preprocess(*ptrs, 1, 1, 128, 64, None) == INVALID
-    assert lib.fa_backward_preprocess(P + 8, P, P, 1, 1, 128, 64, None) == INVALID
-    assert lib.fa_backward_preprocess(P, P, P + 2, 1, 1, 128, 64, None) == INVALID
-    for name, n in (("fa_backward_dkdv", 8), ("fa_backward_dq", 7)):
+    assert lib.fa_backward_preprocess(P + 8, P, P, P, 1, 1, 128, 64, None) == INVALID
+    assert lib.fa_backward_preprocess(P, P + 8, P, P, 1, 1, 128, 64, None) == INVALID
+    assert lib.fa_backward_preprocess(P, P, P + 2, P, 1, 1, 128, 64, None) == INVALID
+    assert lib.fa_backward_preprocess(P, P, P, P + 2, 1, 1, 128, 64, None) == INVALID
+    for name, n, stats in (("fa_backward_dkdv", 7, (4,)), ("fa_backward_dq", 6, (4,))):
         fn = getattr(lib, name)
         assert fn(*([P] * n), 1, 1, 128, 32, 0.1, 0, None) == UNSUPPORTED
         assert fn(*([P] * n), 1, 1, 128, 64, float("nan"), 0, None) == INVALID
@@ -132,16 +134,15 @@ def test_backward_passes_reject_bad_arguments(lib):
             ptrs = [P] * n
             ptrs[i] = None
             assert fn(*ptrs, 1, 1, 128, 64, 0.1, 1, None) == INVALID
-        stats = (4, 5)                       # LSE and workspace come 5th and 6th
-        for i in range(n):
+        for i in range(n):                  # workspace (5th) needs 4-byte, tensors 16-byte alignment
             ptrs = [P] * n
             ptrs[i] = P + (2 if i in stats else 8)
             assert fn(*ptrs, 1, 1, 128, 64, 0.1, 1, None) == INVALID
 
 
 def test_workspace_bytes(lib):
-    assert lib.fa_backward_workspace_bytes(2, 16, 8192, 64) == 2 * 16 * 8192 * 4
-    assert lib.fa_backward_workspace_bytes(1, 1, 1, 128) == 4
+    assert lib.fa_backward_workspace_bytes(2, 16, 8192, 64) == 2 * 2 * 16 * 8192 * 4
+    assert lib.fa_backward_workspace_bytes(1, 1, 1, 128) == 8
     assert lib.fa_backward_workspace_bytes(0, 16, 8192, 64) == 0
     assert lib.fa_backward_workspace_bytes(2, 16, 8192, 96) == 0
 
