@@ -139,8 +139,8 @@ def cpu_baseline(w, host, got, min_seconds=10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -239,6 +239,7 @@ def main():
         "config": {"workload": "fwd+bwd causal bf16 [B,N,H,d]=[2,8192,16,64], scale 1/8, seeded N(0,1)",
                    "B": B, "N": N, "H": H, "d": d, "causal": True, "scale": w.scale},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roof,
         "breakdown": {
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "fwd_tflops": round(F / (fwd_ms * 1e-3) / 1e12, 1),
