@@ -45,7 +45,7 @@ struct BwdArgs {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  int H, N, ntiles;
+  int H, N, ntiles, BH;
   int64_t bhn;        // B*H*N
   float c;            // scale * log2(e)
   float scale;
@@ -145,12 +145,17 @@ __device__ __forceinline__ void store_row_frags(__bf16* row, const f32x16* acc, 
 }
 
 // ------------------------------------------------------------------ dK, dV pass
+// Issue the score products of the next tile before the exp/dS work of the
+// current one (more registers, fewer waves per SIMD) or not.
+constexpr bool kDkdvPipeline = false;
+constexpr bool kDqPipeline = false;
+
 constexpr int kKeysPerWg = 128;   // 4 waves x 32 keys
 constexpr int kBq = 32;           // queries per step
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr bool PIPE = D == 64;            // score products of the next tile run ahead
+__global__ __launch_bounds__(256, D == 64 ? ((kDkdvPipeline || !CAUSAL) ? 2 : 3) : 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr bool PIPE = kDkdvPipeline && D == 64;
   constexpr int NSLOT = PIPE ? 3 : 2;
   constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
   constexpr int TILE = kBq * RB;            // one Q or dO tile
@@ -160,9 +165,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / a.ntiles;
-  const int kt = L - bh * a.ntiles;          // low key tiles see the most queries: run first
+  int bh, kt;
+  tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, false, bh, kt);   // low key tiles see the most queries
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.N;
   const int64_t rs = (int64_t)a.H * D;
@@ -315,10 +319,10 @@ constexpr int kQPerWg = 128;   // 4 waves x 32 queries
 constexpr int kBk = 64;        // keys per step
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
-  // Three K and three V slots: step t reads tiles t and t+1 while tile t+2 is
-  // being copied.
-  constexpr int NS = 3;
+__global__ __launch_bounds__(256, kDqPipeline ? 2 : 3) void bwd_dq_kernel(BwdArgs a) {
+  // Pipelined: three K and three V slots (step t reads tiles t and t+1 while
+  // tile t+2 is being copied); otherwise two of each.
+  constexpr int NS = kDqPipeline ? 3 : 2;
   constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
   constexpr int TILE = kBk * RB;
   constexpr int CPW = TILE / 1024 / 4;
@@ -328,9 +332,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / a.ntiles;
-  const int qtile = a.ntiles - 1 - (L - bh * a.ntiles);   // heaviest (causal) first
+  int bh, qtile;
+  tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, true, bh, qtile);
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.N;
   const int64_t rs = (int64_t)a.H * D;
@@ -413,35 +416,61 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     else update(std::false_type{}, kslot(t), j, sacc, pacc, k0);
   };
 
-  // Software pipeline over 32-key units: the score products of the next unit
-  // (the other half of this tile, or the first half of tile t+1, which was
-  // copied one step ahead) are issued before the dS work of the current unit.
-  // Step t: copies of tile t+2, then units (t, 0) and (t, 1).  On the last
-  // step the look-ahead reads a stale slot and its result is unused.
-  auto step = [&](int t, f32x16& sa, f32x16& pa, f32x16& sb, f32x16& pb2) {
+  if constexpr (kDqPipeline) {
+    // Software pipeline over 32-key units: the score products of the next unit
+    // (the other half of this tile, or the first half of tile t+1, which was
+    // copied one step ahead) are issued before the dS work of the current unit.
+    // Step t: copies of tile t+2, then units (t, 0) and (t, 1).  On the last
+    // step the look-ahead reads a stale slot and its result is unused.
+    auto step = [&](int t, f32x16& sa, f32x16& pa, f32x16& sb, f32x16& pb2) {
+      wait_vmem();
+      __syncthreads();
+      if (t + 2 < nkt) {
+        stage_rows(a.k, t + 2, kslot(t + 2));
+        stage_rows(a.v, t + 2, vslot(t + 2));
+      }
+      if (CAUSAL && t * kBk > qw0 + 31) return;   // this and later tiles lie past the wave's rows
+      scores(kslot(t), vslot(t), 1, sb, pb2);
+      update_sub(t, 0, sa, pa);
+      scores(kslot(t + 1), vslot(t + 1), 0, sa, pa);
+      update_sub(t, 1, sb, pb2);
+    };
+    stage_rows(a.k, 0, kslot(0));
+    stage_rows(a.v, 0, vslot(0));
+    if (nkt > 1) {
+      stage_rows(a.k, 1, kslot(1));
+      stage_rows(a.v, 1, vslot(1));
+    }
     wait_vmem();
     __syncthreads();
-    if (t + 2 < nkt) {
-      stage_rows(a.k, t + 2, kslot(t + 2));
-      stage_rows(a.v, t + 2, vslot(t + 2));
+    f32x16 sa, pa, sb, pb2;
+    scores(kslot(0), vslot(0), 0, sa, pa);
+    for (int t = 0; t < nkt; ++t) step(t, sa, pa, sb, pb2);
+  } else {
+    // Double-buffered K and V of the same tile; step t copies tile t+1 while it
+    // works through the two 32-key units of tile t.
+    stage_rows(a.k, 0, kslot(0));
+    stage_rows(a.v, 0, vslot(0));
+    for (int t = 0; t < nkt; ++t) {
+      wait_vmem();
+      __syncthreads();
+      if (t + 1 < nkt) {
+        stage_rows(a.k, t + 1, kbuf + ((t + 1) & 1) * TILE);
+        stage_rows(a.v, t + 1, vbuf + ((t + 1) & 1) * TILE);
+      }
+      if (CAUSAL && t * kBk > qw0 + 31) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f32x16 sc, pc;
+        scores(kbuf + (t & 1) * TILE, vbuf + (t & 1) * TILE, j, sc, pc);
+        const int k0 = t * kBk;
+        if (CAUSAL && k0 + 32 * j > qw0 + 31) break;
+        const bool masked = (k0 + 32 * j + 32 > N) || (CAUSAL && k0 + 32 * j + 31 > qw0);
+        if (__builtin_expect(masked, 0)) update(std::true_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
+        else update(std::false_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
+      }
     }
-    if (CAUSAL && t * kBk > qw0 + 31) return;   // this and later tiles lie past the wave's rows
-    scores(kslot(t), vslot(t), 1, sb, pb2);
-    update_sub(t, 0, sa, pa);
-    scores(kslot(t + 1), vslot(t + 1), 0, sa, pa);
-    update_sub(t, 1, sb, pb2);
-  };
-  stage_rows(a.k, 0, kslot(0));
-  stage_rows(a.v, 0, vslot(0));
-  if (nkt > 1) {
-    stage_rows(a.k, 1, kslot(1));
-    stage_rows(a.v, 1, vslot(1));
   }
-  wait_vmem();
-  __syncthreads();
-  f32x16 sa, pa, sb, pb2;
-  scores(kslot(0), vslot(0), 0, sa, pa);
-  for (int t = 0; t < nkt; ++t) step(t, sa, pa, sb, pb2);
 
   if (myq < N) store_row_frags<D>(a.dq + base + (int64_t)myq * rs, dq, hh, a.scale);
 }
@@ -489,6 +518,7 @@ BwdArgs make_args(const void* q, const void* k, const void* v, const void* o, co
   a.H = s.H;
   a.N = s.N;
   a.bhn = (int64_t)s.B * s.H * s.N;
+  a.BH = s.B * s.H;
   a.c = s.scale * kLog2e;
   a.scale = s.scale;
   return a;

@@ -148,4 +148,34 @@ __device__ __forceinline__ int xcd_remap(int id, int count) {
   return x * q + (x < r ? x : r) + slot;
 }
 
+// Maps a hardware workgroup id to (head index bh, tile index) for a grid of
+// `ntiles` tiles per head and `bhcount` heads.  Workgroups are dealt to the 8
+// XCDs round-robin (id % 8).  When the head count is a multiple of 8, every XCD
+// gets bhcount/8 whole heads, whose K/V rows then share that XCD's L2.  Under
+// a causal mask the tiles of one XCD go out heaviest first across its heads
+// (longest-processing-time order, so no CU is left with a tail of heavy tiles);
+// otherwise head by head.  `heavy_high`: the highest tile index carries the
+// most work (query tiles that see the most keys); otherwise the lowest (key
+// tiles seen by the most queries).
+__device__ __forceinline__ void tile_of(int id, int ntiles, int bhcount, bool causal, bool heavy_high,
+                                        int& bh, int& tile) {
+  int rank;
+  if ((bhcount & 7) == 0) {
+    const int x = id & 7, s = id >> 3;
+    const int hpx = bhcount >> 3;
+    if (causal) {
+      bh = x * hpx + s % hpx;
+      rank = s / hpx;
+    } else {
+      bh = x * hpx + s / ntiles;
+      rank = s - (s / ntiles) * ntiles;
+    }
+  } else {
+    const int L = xcd_remap(id, ntiles * bhcount);
+    bh = L / ntiles;
+    rank = L - bh * ntiles;
+  }
+  tile = heavy_high ? ntiles - 1 - rank : rank;
+}
+
 }  // namespace fa

@@ -33,8 +33,8 @@
 //  * Causal: tiles above the diagonal are never visited; waves whose 32 rows
 //    cannot see any key of a step skip it; only steps that straddle the
 //    diagonal (or the ragged end of the keys) evaluate the mask.
-//  * Workgroups are renumbered per XCD so one head's query tiles share an L2,
-//    and causal query tiles run heaviest first.
+//  * Workgroups are renumbered per XCD so whole heads share an L2; causal
+//    query tiles go out heaviest first across the heads of an XCD.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -48,6 +48,12 @@ constexpr int kBr = 32 * kWaves;   // query rows per workgroup
 constexpr int kBc = 64;            // keys per step
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kSumLimit = 65536.0f;
+// Issue the score product of the next tile before the softmax of the current
+// one (more registers, fewer waves per SIMD) or not (more waves per SIMD hide
+// the latency instead).  Measured on MI355X: head size 128 gains from the
+// pipeline at 2 waves per SIMD; head size 64 runs faster unpipelined at 3.
+template <int D>
+constexpr bool fwd_pipelined() { return D == 128; }
 
 struct FwdArgs {
   const __bf16* q;
@@ -55,12 +61,12 @@ struct FwdArgs {
   const __bf16* v;
   __bf16* o;
   float* lse;
-  int H, N, nqt;
+  int H, N, nqt, BH;
   float c;   // scale * log2(e)
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, fwd_pipelined<D>() ? 2 : 3) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int KS = D / 16;           // k-steps of the score product
   constexpr int DT = D / 32;           // 32-wide output tiles
@@ -73,9 +79,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / a.nqt;
-  const int qt = a.nqt - 1 - (L - bh * a.nqt);
+  int bh, qt;
+  tile_of(blockIdx.x, a.nqt, a.BH, CAUSAL, true, bh, qt);
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.N;
   const int64_t rs = (int64_t)a.H * D;                       // row stride (elements)
@@ -259,41 +264,63 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Software pipeline: the score product of tile t+1 is issued before the
   // softmax of tile t, so the matrix cores work on it while the vector unit
   // exponentiates; tile t's P V product follows.
-  // One step: copies for later tiles, next tile's scores into `snext`, then
-  // softmax and P V of tile kt from `scur`.
-  auto step = [&](int kt, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+  if constexpr (fwd_pipelined<D>()) {
+    // One step: copies for later tiles, next tile's scores into `snext`, then
+    // softmax and P V of tile kt from `scur`.
+    auto step = [&](int kt, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+      wait_vmem();
+      __syncthreads();
+      if (kt + 2 < nkt) stage_rows(Kg, kt + 2, kbuf + (kt & 1) * TILE);
+      if (kt + 1 < nkt) stage_rows(Vg, kt + 1, vbuf + ((kt + 1) & 1) * TILE);
+      const int k0 = kt * kBc;
+      // All keys of this step lie beyond this wave's rows: nothing left to add.
+      if (CAUSAL && k0 > qw0 + 31) return;
+      // Scores of the next tile (on the last step this reads a stale buffer and
+      // the result is never used).
+      scores(kbuf + ((kt + 1) & 1) * TILE, snext);
+      const char* vb = vbuf + (kt & 1) * TILE;
+      const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
+      if (__builtin_expect(masked, 0)) softmax_pv(std::true_type{}, scur, vb, k0);
+      else softmax_pv(std::false_type{}, scur, vb, k0);
+    };
+    // Software pipeline: the score product of tile t+1 is issued before the
+    // softmax of tile t, so the matrix cores work on it while the vector unit
+    // exponentiates; tile t's P V product follows.
+    stage_rows(Kg, 0, kbuf);
+    stage_rows(Vg, 0, vbuf);
+    if (nkt > 1) stage_rows(Kg, 1, kbuf + TILE);
     wait_vmem();
     __syncthreads();
-    if (kt + 2 < nkt) stage_rows(Kg, kt + 2, kbuf + (kt & 1) * TILE);
-    if (kt + 1 < nkt) stage_rows(Vg, kt + 1, vbuf + ((kt + 1) & 1) * TILE);
-    const int k0 = kt * kBc;
-    // All keys of this step lie beyond this wave's rows: nothing left to add.
-    if (CAUSAL && k0 > qw0 + 31) return;
-    // Scores of the next tile (on the last step this reads a stale buffer and
-    // the result is never used).
-    scores(kbuf + ((kt + 1) & 1) * TILE, snext);
-    const char* vb = vbuf + (kt & 1) * TILE;
-    const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
-    if (__builtin_expect(masked, 0)) softmax_pv(std::true_type{}, scur, vb, k0);
-    else softmax_pv(std::false_type{}, scur, vb, k0);
-  };
-
-  // Software pipeline: the score product of tile t+1 is issued before the
-  // softmax of tile t, so the matrix cores work on it while the vector unit
-  // exponentiates; tile t's P V product follows.
-  stage_rows(Kg, 0, kbuf);
-  stage_rows(Vg, 0, vbuf);
-  if (nkt > 1) stage_rows(Kg, 1, kbuf + TILE);
-  wait_vmem();
-  __syncthreads();
-  f32x16 sa[2], sb[2];
-  scores(kbuf, sa);
-  int kt = 0;
-  for (; kt + 1 < nkt; kt += 2) {
-    step(kt, sa, sb);
-    step(kt + 1, sb, sa);
+    f32x16 sa[2], sb[2];
+    scores(kbuf, sa);
+    int kt = 0;
+    for (; kt + 1 < nkt; kt += 2) {
+      step(kt, sa, sb);
+      step(kt + 1, sb, sa);
+    }
+    if (kt < nkt) step(kt, sa, sb);
+  } else {
+    // Double-buffered K and V of the same tile: step t copies tile t+1 while
+    // it computes scores, softmax and P V of tile t.
+    stage_rows(Kg, 0, kbuf);
+    stage_rows(Vg, 0, vbuf);
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int cur = kt & 1;
+      wait_vmem();
+      __syncthreads();
+      if (kt + 1 < nkt) {
+        stage_rows(Kg, kt + 1, kbuf + (cur ^ 1) * TILE);
+        stage_rows(Vg, kt + 1, vbuf + (cur ^ 1) * TILE);
+      }
+      const int k0 = kt * kBc;
+      if (CAUSAL && k0 > qw0 + 31) continue;
+      f32x16 sc[2];
+      scores(kbuf + cur * TILE, sc);
+      const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
+      if (__builtin_expect(masked, 0)) softmax_pv(std::true_type{}, sc, vbuf + cur * TILE, k0);
+      else softmax_pv(std::false_type{}, sc, vbuf + cur * TILE, k0);
+    }
   }
-  if (kt < nkt) step(kt, sa, sb);
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
   const float l = sum_halves(l_part);
@@ -333,6 +360,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   a.H = s.H;
   a.N = s.N;
   a.nqt = (s.N + kBr - 1) / kBr;
+  a.BH = s.B * s.H;
   a.c = s.scale * kLog2e;
   const int BH = s.B * s.H;
   if (s.d == 64) return s.causal ? launch<64, true>(a, BH, stream) : launch<64, false>(a, BH, stream);
