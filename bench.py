@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the fused exact-attention hot path on one MI355X.
 
-One step = one forward (fa_forward) and one backward (fa_backward_preprocess,
-fa_backward_dkdv, fa_backward_dq - exactly what fa_backward runs) of bf16
+One step = one forward (fa_forward) and one backward (fa_backward_preprocess
+then fa_backward_dqdkdv - exactly what fa_backward runs) of bf16
 causal attention on the forward+backward workload [B, N, H, d] = [2, 8192, 16,
 64], scale 1/8, inputs seeded N(0, 1) and already resident in HBM.
 
@@ -184,23 +184,20 @@ def main():
         fa.fa_backward_preprocess(o, do, lse, ws)
         if evs:
             evs[2].record(st)
-        fa.fa_backward_dkdv(q, k, v, do, ws, dk, dv, w.scale, True)
+        fa.fa_backward_dqdkdv(q, k, v, do, ws, dq, dk, dv, w.scale, True)
         if evs:
             evs[3].record(st)
-        fa.fa_backward_dq(q, k, v, do, ws, dq, w.scale, True)
-        if evs:
-            evs[4].record(st)
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+    names = ["fwd", "bwd_preprocess", "bwd_dqdkdv"]
     per = {n: [events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)] for j, n in enumerate(names)}
     avg = {n: sum(x) / len(x) for n, x in per.items()}
     ms_step = wall * 1e3 / args.steps
@@ -209,12 +206,13 @@ def main():
     Fb = 2.5 * F
     value = (F + Fb) / (ms_step * 1e-3) / 1e12
     fwd_ms = avg["fwd"]
-    bwd_ms = avg["bwd_preprocess"] + avg["bwd_dkdv"] + avg["bwd_dq"]
+    bwd_ms = avg["bwd_preprocess"] + avg["bwd_dqdkdv"]
     pairs = B * H * N * N / 2.0                      # visible (query, key) pairs, causal
     alg = {   # algorithmic work of one launch of each kernel
         "fwd": ("mfma", 4.0 * d * pairs),            # S = QK^T and O += PV
-        "bwd_dkdv": ("mfma", 8.0 * d * pairs),       # S, dP, dV += P^T dO, dK += dS^T Q
-        "bwd_dq": ("mfma", 6.0 * d * pairs),         # S, dP, dQ += dS K
+        # dK/dV tiles (S, dP, dV += P^T dO, dK += dS^T Q) and dQ tiles (S, dP,
+        # dQ += dS K) in one grid: 8d + 6d FLOPs per visible pair
+        "bwd_dqdkdv": ("mfma", 14.0 * d * pairs),
         "bwd_preprocess": ("hbm", 2.0 * B * N * H * d * 2 + 12.0 * B * H * N),  # read O, dO, LSE; write D, -LSE log2 e
     }
     dom = max(avg, key=avg.get)

@@ -14,6 +14,7 @@ from __future__ import annotations
 import torch
 
 from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_dkdv, fa_backward_dq,  # noqa: F401
+                   fa_backward_dqdkdv,
                    fa_backward_preprocess, fa_backward_workspace_bytes, fa_forward,
                    fa_status_string, load)
 

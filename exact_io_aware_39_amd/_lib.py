@@ -45,9 +45,9 @@ def load() -> ctypes.CDLL:
         fn.argtypes, fn.restype = args, I
     lib.fa_backward_preprocess.argtypes = [P, P, P, P, I, I, I, I, P]
     lib.fa_backward_preprocess.restype = I
-    for name in ("fa_backward_dkdv", "fa_backward_dq"):
+    for name, nptr in (("fa_backward_dqdkdv", 8), ("fa_backward_dkdv", 7), ("fa_backward_dq", 6)):
         fn = getattr(lib, name)
-        fn.argtypes = [P] * (7 if name == "fa_backward_dkdv" else 6) + [I, I, I, I, F, I, P]
+        fn.argtypes = [P] * nptr + [I, I, I, I, F, I, P]
         fn.restype = I
     lib.fa_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.fa_backward_workspace_bytes.restype = S
@@ -130,6 +130,17 @@ def fa_backward_preprocess(o, do, lse, workspace, stream=None):
     _check_ws(workspace, B, H, N, d)
     _call("fa_backward_preprocess", load().fa_backward_preprocess(
         _ptr(o), _ptr(do), _ptr(lse), _ptr(workspace), B, H, N, d, _stream(stream)))
+
+
+def fa_backward_dqdkdv(q, k, v, do, workspace, dq, dk, dv, scale: float, causal: bool, stream=None):
+    """fa_backward_dqdkdv: dQ, dK and dV in one launch from the preprocessed workspace."""
+    B, N, H, d = _shape(q)
+    _check((q, k, v, do, dq, dk, dv), torch.bfloat16)
+    _check((workspace,), torch.float32)
+    _check_ws(workspace, B, H, N, d)
+    _call("fa_backward_dqdkdv", load().fa_backward_dqdkdv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, H, N, d, float(scale), int(bool(causal)), _stream(stream)))
 
 
 def fa_backward_dkdv(q, k, v, do, workspace, dk, dv, scale: float, causal: bool, stream=None):

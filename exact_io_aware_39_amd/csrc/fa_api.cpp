@@ -88,6 +88,17 @@ fa_status fa_backward_preprocess(const void* O, const void* dO, const float* LSE
   return to_status(fa::launch_bwd_pre_bf16(O, dO, LSE, workspace, s, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_backward_dqdkdv(const void* Q, const void* K, const void* V, const void* dO,
+                             const float* workspace, void* dQ, void* dK, void* dV,
+                             int B, int H, int N, int d, float scale, int causal, void* stream) {
+  fa_status st = check_common(B, H, N, d, scale, causal);
+  if (st == FA_OK) st = check_tensors({Q, K, V, dO, dQ, dK, dV}, {workspace});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal};
+  return to_status(fa::launch_bwd_dqdkdv_bf16(Q, K, V, dO, workspace, dQ, dK, dV, s,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
                            const float* workspace, void* dK, void* dV,
                            int B, int H, int N, int d, float scale, int causal, void* stream) {

@@ -23,6 +23,8 @@
 //                 rows resident); walks the key tiles they can see.  S^T and
 //                 dP^T have the query as the lane, so the row statistics are
 //                 one scalar per lane, and dS^T feeds dQ^T += K^T dS^T directly.
+// fa_backward runs 2 and 3 as one grid (bwd_fused) ordered heaviest first, so
+// the two passes share one tail; the split entry points launch them apart.
 // Both passes stage their streamed tiles with buffer -> LDS copies into a ring
 // of LDS slots and, at head size 64, software-pipeline the two score-like
 // products of the next tile ahead of the exp / dS work of the current one.
@@ -153,20 +155,24 @@ constexpr bool kDqPipeline = false;
 constexpr int kKeysPerWg = 128;   // 4 waves x 32 keys
 constexpr int kBq = 32;           // queries per step
 
+template <int D>
+constexpr int dkdv_lds_bytes() {
+  return ((kDkdvPipeline && D == 64) ? 3 : 2) * (2 * kBq * D * 2 + 512);
+}
+
+// dK, dV of key tile kt of head bh (one workgroup).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D == 64 ? ((kDkdvPipeline || !CAUSAL) ? 2 : 3) : 1) void bwd_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char* smem) {
   constexpr bool PIPE = kDkdvPipeline && D == 64;
   constexpr int NSLOT = PIPE ? 3 : 2;
   constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
   constexpr int TILE = kBq * RB;            // one Q or dO tile
   constexpr int CPW = TILE / 1024 / 4;      // 1 KB copies per wave per tile
   constexpr int SLOT = 2 * TILE + 512;      // Q, dO, then 64 floats of -LSE log2 e and of D
-  __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
+  static_assert(NSLOT * SLOT == dkdv_lds_bytes<D>(), "LDS layout");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
-  int bh, kt;
-  tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, false, bh, kt);   // low key tiles see the most queries
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.N;
   const int64_t rs = (int64_t)a.H * D;
@@ -318,22 +324,26 @@ __global__ __launch_bounds__(256, D == 64 ? ((kDkdvPipeline || !CAUSAL) ? 2 : 3)
 constexpr int kQPerWg = 128;   // 4 waves x 32 queries
 constexpr int kBk = 64;        // keys per step
 
+template <int D>
+constexpr int dq_lds_bytes() {
+  return 2 * (kDqPipeline ? 3 : 2) * kBk * D * 2;
+}
+
+// dQ of query tile qtile of head bh (one workgroup).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, kDqPipeline ? 2 : 3) void bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, char* smem) {
   // Pipelined: three K and three V slots (step t reads tiles t and t+1 while
   // tile t+2 is being copied); otherwise two of each.
   constexpr int NS = kDqPipeline ? 3 : 2;
   constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
   constexpr int TILE = kBk * RB;
   constexpr int CPW = TILE / 1024 / 4;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];   // K slots, then V slots
+  static_assert(2 * NS * TILE == dq_lds_bytes<D>(), "LDS layout");
   char* const kbuf = smem;
   char* const vbuf = smem + NS * TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
-  int bh, qtile;
-  tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, true, bh, qtile);
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.N;
   const int64_t rs = (int64_t)a.H * D;
@@ -475,6 +485,89 @@ __global__ __launch_bounds__(256, kDqPipeline ? 2 : 3) void bwd_dq_kernel(BwdArg
   if (myq < N) store_row_frags<D>(a.dq + base + (int64_t)myq * rs, dq, hh, a.scale);
 }
 
+// ------------------------------------------------------------------ kernels
+template <int D, bool CAUSAL>
+constexpr int bwd_min_waves() {
+  return D == 64 ? ((kDkdvPipeline || !CAUSAL) ? 2 : 3) : 1;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL>())) void bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[dkdv_lds_bytes<D>()];
+  int bh, kt;
+  tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, false, bh, kt);   // low key tiles see the most queries
+  dkdv_tile<D, CAUSAL>(a, bh, kt, smem);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, kDqPipeline ? 2 : 3) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[dq_lds_bytes<D>()];
+  int bh, qt;
+  tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, true, bh, qt);
+  dq_tile<D, CAUSAL>(a, bh, qt, smem);
+}
+
+// Both passes in one grid (a.ntiles key tiles and as many query tiles per head,
+// both 128 rows), so that the light tiles of one pass fill the other's tail.
+// Every XCD takes whole heads when the head count is a multiple of 8 (else the
+// whole grid is one group) and hands out its tasks heaviest first by FLOPs.
+// Under a causal mask the task costs, in units of 64x128 visible pairs times
+// the FLOPs per pair, are 8 (2 (nt - kt) - 1) for key tile kt (4 GEMMs) and
+// 6 (2 qt + 1) for query tile qt (3 GEMMs): two arithmetic sequences whose
+// values never coincide, so the rank-r task is found by a binary search on the
+// cost.  Without a mask the dK/dV tasks (the heavier ones) go first.
+__device__ __forceinline__ void fused_task(int id, int nt, int bhcount, bool causal,
+                                           bool& is_kv, int& bh, int& tile) {
+  int group, rank, hpg;
+  if ((bhcount & 7) == 0) {
+    group = id & 7;
+    rank = id >> 3;
+    hpg = bhcount >> 3;
+  } else {
+    group = 0;
+    rank = id;
+    hpg = bhcount;
+  }
+  int which;   // task index inside its pass for this group: tile * hpg + head
+  if (!causal) {
+    is_kv = rank < nt * hpg;
+    which = is_kv ? rank : rank - nt * hpg;
+    bh = group * hpg + which % hpg;
+    tile = which / hpg;
+    return;
+  }
+  // Number of tasks with cost >= w.
+  auto count_ge = [&](int w) {
+    const int kvmax = 8 * (2 * nt - 1), dqmax = 6 * (2 * nt - 1);
+    const int kv = w > kvmax ? 0 : min(nt, (kvmax - w) / 16 + 1);
+    const int dq = w > dqmax ? 0 : min(nt, (dqmax - w) / 12 + 1);
+    return (kv + dq) * hpg;
+  };
+  // Largest w with count_ge(w) > rank: the cost of the rank-r task.
+  int lo = 1, hi = 8 * (2 * nt - 1);
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (count_ge(mid) > rank) lo = mid;
+    else hi = mid - 1;
+  }
+  const int w = lo;
+  const int pos = rank - count_ge(w + 1);   // position among the hpg tasks of cost w
+  is_kv = (w % 16) == 8;
+  tile = is_kv ? nt - (w / 8 + 1) / 2 : (w / 6 - 1) / 2;
+  bh = group * hpg + pos;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL>())) void bwd_fused_kernel(BwdArgs a) {
+  constexpr int LDS = dkdv_lds_bytes<D>() > dq_lds_bytes<D>() ? dkdv_lds_bytes<D>() : dq_lds_bytes<D>();
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
+  bool is_kv;
+  int bh, tile;
+  fused_task(blockIdx.x, a.ntiles, a.BH, CAUSAL, is_kv, bh, tile);
+  if (is_kv) dkdv_tile<D, CAUSAL>(a, bh, tile, smem);
+  else dq_tile<D, CAUSAL>(a, bh, tile, smem);
+}
+
 template <int D>
 hipError_t run_pre(const BwdArgs& a, int B, hipStream_t st) {
   const int64_t rows = (int64_t)B * a.N * a.H;
@@ -499,6 +592,15 @@ hipError_t run_dq(BwdArgs a, int BH, bool causal, hipStream_t st) {
   const dim3 grid(a.ntiles * BH);
   if (causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t run_fused(BwdArgs a, int BH, bool causal, hipStream_t st) {
+  a.ntiles = (a.N + kKeysPerWg - 1) / kKeysPerWg;   // == query tiles (both 128 rows)
+  const dim3 grid(2 * a.ntiles * BH);
+  if (causal) hipLaunchKernelGGL((bwd_fused_kernel<D, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((bwd_fused_kernel<D, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -541,6 +643,15 @@ hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, con
                    : run_dkdv<128>(a, BH, s.causal != 0, stream);
 }
 
+hipError_t launch_bwd_dqdkdv_bf16(const void* q, const void* k, const void* v, const void* dout,
+                                  const float* ws, void* dq, void* dk, void* dv, const AttnShape& s,
+                                  hipStream_t stream) {
+  const BwdArgs a = make_args(q, k, v, nullptr, dout, nullptr, const_cast<float*>(ws), dq, dk, dv, s);
+  const int BH = s.B * s.H;
+  return s.d == 64 ? run_fused<64>(a, BH, s.causal != 0, stream)
+                   : run_fused<128>(a, BH, s.causal != 0, stream);
+}
+
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout,
                               const float* ws, void* dq, const AttnShape& s, hipStream_t stream) {
   const BwdArgs a = make_args(q, k, v, nullptr, dout, nullptr, const_cast<float*>(ws), dq, nullptr, nullptr, s);
@@ -553,9 +664,8 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
                            float* ws, const AttnShape& s, hipStream_t stream) {
   hipError_t e = launch_bwd_pre_bf16(o, dout, lse, ws, s, stream);
-  if (e == hipSuccess) e = launch_bwd_dkdv_bf16(q, k, v, dout, ws, dk, dv, s, stream);
-  if (e == hipSuccess) e = launch_bwd_dq_bf16(q, k, v, dout, ws, dq, s, stream);
-  return e;
+  if (e != hipSuccess) return e;
+  return launch_bwd_dqdkdv_bf16(q, k, v, dout, ws, dq, dk, dv, s, stream);
 }
 
 }  // namespace fa

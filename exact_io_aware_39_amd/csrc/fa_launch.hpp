@@ -26,6 +26,9 @@ hipError_t launch_bwd_pre_bf16(const void* o, const void* dout, const float* lse
 hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout,
                                 const float* ws, void* dk, void* dv, const AttnShape& s,
                                 hipStream_t stream);
+hipError_t launch_bwd_dqdkdv_bf16(const void* q, const void* k, const void* v, const void* dout,
+                                  const float* ws, void* dq, void* dk, void* dv, const AttnShape& s,
+                                  hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout,
                               const float* ws, void* dq, const AttnShape& s, hipStream_t stream);
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,

@@ -101,14 +101,20 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
  *   fa_backward_preprocess  fills `workspace` with D_i = sum_c dO_ic O_ic and
  *                           -LSE_i log2(e) (two fp32 [B, H, N] arrays, in that
  *                           order);
- *   fa_backward_dkdv        dK = scale dS^T Q and dV = P^T dO;
- *   fa_backward_dq          dQ = scale dS K;
- * the last two read the workspace written by the preprocess.  They only read
- * shared inputs, so once the preprocess has completed they may run
- * concurrently on different streams.
+ *   fa_backward_dqdkdv      dQ, dK and dV in one launch (what fa_backward runs
+ *                           after the preprocess: both passes share one grid,
+ *                           heaviest tiles first);
+ *   fa_backward_dkdv        dK = scale dS^T Q and dV = P^T dO alone;
+ *   fa_backward_dq          dQ = scale dS K alone;
+ * the last three read the workspace written by the preprocess.  They only
+ * read shared inputs, so once the preprocess has completed the separate dK/dV
+ * and dQ passes may also run concurrently on different streams.
  */
 fa_status fa_backward_preprocess(const void* O, const void* dO, const float* LSE, float* workspace,
                                  int B, int H, int N, int d, void* stream);
+fa_status fa_backward_dqdkdv(const void* Q, const void* K, const void* V, const void* dO,
+                             const float* workspace, void* dQ, void* dK, void* dV,
+                             int B, int H, int N, int d, float scale, int causal, void* stream);
 fa_status fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
                            const float* workspace, void* dK, void* dV,
                            int B, int H, int N, int d, float scale, int causal, void* stream);

@@ -38,6 +38,8 @@ def lib():
         getattr(lib, name).restype = i
     lib.fa_backward_preprocess.argtypes = [vp] * 4 + [i] * 4 + [vp]
     lib.fa_backward_preprocess.restype = i
+    lib.fa_backward_dqdkdv.argtypes = [vp] * 8 + [i] * 4 + [f, i, vp]
+    lib.fa_backward_dqdkdv.restype = i
     lib.fa_backward_dkdv.argtypes = [vp] * 7 + [i] * 4 + [f, i, vp]
     lib.fa_backward_dkdv.restype = i
     lib.fa_backward_dq.argtypes = [vp] * 6 + [i] * 4 + [f, i, vp]
@@ -52,7 +54,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_f32",
-        "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq",
+        "fa_backward_preprocess", "fa_backward_dqdkdv", "fa_backward_dkdv", "fa_backward_dq",
         "fa_backward_workspace_bytes", "fa_status_string"])
 
 
@@ -125,7 +127,8 @@ def test_backward_passes_reject_bad_arguments(lib):
     assert lib.fa_backward_preprocess(P, P + 8, P, P, 1, 1, 128, 64, None) == INVALID
     assert lib.fa_backward_preprocess(P, P, P + 2, P, 1, 1, 128, 64, None) == INVALID
     assert lib.fa_backward_preprocess(P, P, P, P + 2, 1, 1, 128, 64, None) == INVALID
-    for name, n, stats in (("fa_backward_dkdv", 7, (4,)), ("fa_backward_dq", 6, (4,))):
+    for name, n, stats in (("fa_backward_dqdkdv", 8, (4,)), ("fa_backward_dkdv", 7, (4,)),
+                           ("fa_backward_dq", 6, (4,))):
         fn = getattr(lib, name)
         assert fn(*([P] * n), 1, 1, 128, 32, 0.1, 0, None) == UNSUPPORTED
         assert fn(*([P] * n), 1, 1, 128, 64, float("nan"), 0, None) == INVALID
