@@ -79,6 +79,13 @@ def test_small_ragged_fp32(N, d, causal):
     run_and_check((1, N, 2, d), "f32", 4000 + N + d, causal, d ** -0.5, tag="ragged-f32")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_groups_ragged(d, causal):
+    """B*H a multiple of 8 (whole heads per XCD group) with a ragged last tile."""
+    run_and_check((2, 300, 4, d), "bf16", 8008 + d, causal, d ** -0.5, tag="groups")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_d128_midsize(causal):
     run_and_check((1, 2048, 4, 128), "bf16", 5005, causal, 128 ** -0.5, heads=[(0, 1), (0, 3)], tag="d128")

@@ -66,6 +66,13 @@ def test_small_ragged_bf16(N, d, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_groups_ragged(d, causal):
+    """B*H a multiple of 8 (whole heads per XCD group) with a ragged last tile."""
+    run_and_check((2, 300, 4, d), "bf16", 9009 + d, causal, d ** -0.5, tag="groups")
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 33, 200])
 @pytest.mark.parametrize("causal", [False, True])
 def test_small_ragged_fp32(N, d, causal):
