@@ -11,8 +11,10 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three launches on one stream, no atomics (results are bit-reproducible):
-//   1. bwd_pre  : workspace = [D | -LSE log2(e)], streaming O and dO once, so
-//                 that P = exp2(c S + nl) is one FMA and one exp per element.
+//   1. bwd_pre  : workspace = [-D | -LSE log2(e)], streaming O and dO once, so
+//                 that P = exp2(c S + nl) is one FMA and one exp per element,
+//                 and dP - D comes out of the dP product itself (its
+//                 accumulator starts from -D), leaving one multiply for dS.
 //   2. bwd_dkdv : one workgroup per 128 keys (32 per wave, K and V of those
 //                 keys resident in registers); walks the query tiles that can
 //                 see them.  S = Q K^T and dP = dO V^T use 32x32x16 MFMA with
@@ -26,8 +28,10 @@
 // fa_backward runs 2 and 3 as one grid (bwd_fused) ordered heaviest first, so
 // the two passes share one tail; the split entry points launch them apart.
 // Both passes stage their streamed tiles with buffer -> LDS copies into a ring
-// of LDS slots and, at head size 64, software-pipeline the two score-like
-// products of the next tile ahead of the exp / dS work of the current one.
+// of LDS slots.  A software-pipelined form of each loop (the two score-like
+// products of the next tile issued ahead of the exp / dS work of the current
+// one) is kept behind kDkdvPipeline / kDqPipeline; at head size 64 the plain
+// loops at three waves per SIMD measure faster than the pipelined ones at two.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -43,7 +47,7 @@ struct BwdArgs {
   const __bf16* o;
   const __bf16* dout;
   const float* lse;
-  float* ws;          // [D (B*H*N) | -LSE*log2(e) (B*H*N)]
+  float* ws;          // [-D (B*H*N) | -LSE*log2(e) (B*H*N)]
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
     const int64_t h = r % H, bn = r / H;
     const int64_t n = bn % N, b = bn / N;
     const int64_t idx = (b * H + h) * N + n;
-    ws[idx] = acc;
+    ws[idx] = -acc;
     ws[bhn + idx] = -lse[idx] * kLog2e;
   }
 }
@@ -223,9 +227,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
   const uint32_t rfb = row_frag_base<D>(lane);
   const uint32_t tfb = tr_frag_base<D>(lane);
   // S = Q K^T and dP = dO V^T: lane = key, register r = query row 8(r/4) + 4hh + r%4.
+  // The dP product starts from -D of each query row, so pacc ends as dP - D.
   auto scores = [&](const char* slot, f32x16& sacc, f32x16& pacc) {
     sacc = (f32x16){};
-    pacc = (f32x16){};
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 nd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (8 * g4 + 4 * hh) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pacc[4 * g4 + e] = nd[e];
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       sacc = mfma32x32x16(lds_read_b128(slot, rfb ^ (ks << 5)), kf[ks], sacc);
@@ -244,7 +254,6 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
       for (int g = 0; g < 2; ++g) {
         const int g4 = 2 * u + g;
         const f32x4 nl = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + (8 * g4 + 4 * hh) * 4);
-        const f32x4 dd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (8 * g4 + 4 * hh) * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
@@ -255,7 +264,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
             pv = hide ? 0.f : pv;
           }
           p[4 * g + e] = pv;
-          ds[4 * g + e] = pv * (pacc[r] - dd[e]);
+          ds[4 * g + e] = pv * pacc[r];
         }
       }
       const bf16x8 pb = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
@@ -361,7 +370,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
     gf[ks] = *reinterpret_cast<const bf16x8*>(a.dout + base + (int64_t)qc * rs + (2 * ks + hh) * 8);
   }
   const float nl2 = a.ws[a.bhn + (int64_t)bh * N + qc];
-  const float dval = a.ws[(int64_t)bh * N + qc];
+  const float ndval = a.ws[(int64_t)bh * N + qc];   // -D of this lane's query
 
   f32x16 dq[DT];
 #pragma unroll
@@ -387,7 +396,8 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
   // lane = query, register r = key 32 j + 8(r/4) + 4hh + r%4.
   auto scores = [&](const char* kt, const char* vt, int j, f32x16& sacc, f32x16& pacc) {
     sacc = (f32x16){};
-    pacc = (f32x16){};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pacc[r] = ndval;   // so that pacc ends as dP^T - D
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       sacc = mfma32x32x16(lds_read_b128(kt, (rfb ^ (ks << 5)) + 32 * j * RB), qf[ks], sacc);
@@ -409,7 +419,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
           const bool hide = key >= N || (CAUSAL && key > myq);
           pv = hide ? 0.f : pv;
         }
-        ds[e] = pv * (pacc[r] - dval);
+        ds[e] = pv * pacc[r];
       }
       const bf16x8 db = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
       // dQ^T += K^T dS^T (rows d, columns queries)

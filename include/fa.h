@@ -98,9 +98,9 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
 /*
  * The three passes fa_backward runs, in this order, for callers that schedule
  * them themselves (bf16 tensors, same layouts and checks as fa_backward):
- *   fa_backward_preprocess  fills `workspace` with D_i = sum_c dO_ic O_ic and
- *                           -LSE_i log2(e) (two fp32 [B, H, N] arrays, in that
- *                           order);
+ *   fa_backward_preprocess  fills `workspace` with -D_i (D_i = sum_c dO_ic O_ic)
+ *                           and -LSE_i log2(e) (two fp32 [B, H, N] arrays, in
+ *                           that order);
  *   fa_backward_dqdkdv      dQ, dK and dV in one launch (what fa_backward runs
  *                           after the preprocess: both passes share one grid,
  *                           heaviest tiles first);
