@@ -51,15 +51,37 @@ def _compile(src, obj, verbose):
     return obj
 
 
+def _device_asm(src, out, verbose):
+    """gfx950 assembly of one kernel source (what the object file contains)."""
+    cmd = [_hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", src, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {os.path.basename(src)}:\n{r.stderr}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libfa.so next to this file; returns its path."""
+    """Compile every source, check the asm-issued LDS reads in the generated
+    assembly, and link libfa.so next to this file; returns its path."""
+    from . import asm_check
+
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     srcs = _sources()
     objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
-    workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    hips = [s for s in srcs if s.endswith(".hip")]
+    asms = [os.path.join(objdir, os.path.basename(s) + ".s") for s in hips]
+    jobs = [(_compile, so, ob) for so, ob in zip(srcs, objs)] + [(_device_asm, so, a) for so, a in zip(hips, asms)]
+    workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(workers) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(srcs, objs)))
+        list(ex.map(lambda j: j[0](j[1], j[2], verbose), jobs))
+    problems = []
+    for a in asms:
+        problems += asm_check.check_file(a)[0]
+    if problems:
+        raise RuntimeError("asm-issued LDS reads used before their wait:\n" + "\n".join(problems[:20]))
     tmp = OUT + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

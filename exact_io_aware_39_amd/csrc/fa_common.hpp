@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -110,6 +112,67 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, uint32_t off) 
 // by lanes i/4, 4+i/4, 8+i/4, 12+i/4 of that group, in that order.
 __device__ __forceinline__ s16x4 lds_read_tr16(const char* base, uint32_t off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + off));
+}
+
+// Compile-time loop: calls f(std::integral_constant<int, i>) for i in [I, N).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const FA_LDS char*)p;
+}
+
+// ---- LDS reads issued from inline asm
+// The compiler treats the transposing-read builtin as a possible reader of
+// every global -> LDS copy still in flight and drains them all (vmcnt(0))
+// before each one, so copies issued for later tiles would stall the reads of
+// the current tile.  These asm forms are invisible to the compiler's wait
+// counters instead, which puts their ordering in the caller's hands:
+//  * a value read by lds_*_issue may only be used after lds_wait<n>() with n
+//    no larger than the number of asm LDS reads issued after it (LDS returns
+//    in order, so the n most recent reads may still be pending; reads the
+//    compiler issues in between only make the wait stricter), and after
+//    lds_ready() has passed it through (so no use is scheduled earlier);
+//  * the data must already be in LDS and visible (the callers read tiles that
+//    a barrier after s_waitcnt vmcnt has published).
+// The build scans the generated ISA and fails if any instruction touches the
+// destination registers of such a read before a wait that retires it.
+template <uint32_t OFF>
+__device__ __forceinline__ s16x4 lds_tr16_issue(uint32_t addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <uint32_t OFF>
+__device__ __forceinline__ bf16x8 lds_b128_issue(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is a 4-bit field");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
+}
+__device__ __forceinline__ void lds_ready(s16x4& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void lds_ready(bf16x8& x) { asm volatile("" : "+v"(x)); }
+
+// The A operand (tile^T fragment) from a retired pair of transposing reads:
+// the low four k values from r[0], the high four from r[1].
+__device__ __forceinline__ bf16x8 tr_pair_take(s16x4 (&r)[2]) {
+  lds_ready(r[0]);
+  lds_ready(r[1]);
+  const bf16x4 a = __builtin_bit_cast(bf16x4, r[0]), b = __builtin_bit_cast(bf16x4, r[1]);
+  bf16x8 v;
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  return v;
 }
 
 // Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l's

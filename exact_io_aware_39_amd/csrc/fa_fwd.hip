@@ -20,16 +20,20 @@
 //    read ds_read_b64_tr_b16; K fragments are plain 16-byte LDS reads.  Tile
 //    rows are dense with XOR-permuted 16-byte chunks (no bank conflicts for
 //    either read); every fragment address is a lane base XOR a constant.
-//  * K and V tiles are double buffered in LDS and filled by asynchronous
-//    global -> LDS copies (no staging registers); K runs one tile ahead of V
-//    so that step t issues the score product of tile t+1 before the softmax of
-//    tile t (software pipelining: the MFMA latency of S hides under the exp
-//    work) and then tile t's P V product; one barrier per step.
+//  * K and V tiles live in LDS rings filled by asynchronous global -> LDS
+//    copies (no staging registers), one barrier per step.  The loop form
+//    depends on the head size and the mask (fwd_mode): one tile per step at
+//    d = 64; at d = 128 the score product of tile t+1 is issued ahead of the
+//    softmax of tile t, and with a causal mask the P V product of tile t-1 is
+//    deferred into the same step so that both products interleave with the
+//    softmax arithmetic, one product after every exp.
+//  * V^T is read with asm-issued transposing reads: the compiler would wait
+//    for every copy in flight before the builtin form of that read.
 //  * exp is exp2 with scale*log2(e) folded into one FMA.  The reference max is
-//    only moved when a row's max grows by more than 2^8 (RESCALE_LOG2): any
+//    only moved when a row's max grows by more than 2^8 (kRescaleLog2), or,
+//    without a mask, when a row's share of the sum exceeds 2^16: any
 //    finite reference gives the same O and LSE (the final divide uses the same
-//    reference), so this keeps exactness while the O rescale becomes rare;
-//    probabilities stay <= 2^8 before normalisation.
+//    reference), so this keeps exactness while the O rescale becomes rare.
 //  * Causal: tiles above the diagonal are never visited; waves whose 32 rows
 //    cannot see any key of a step skip it; only steps that straddle the
 //    diagonal (or the ragged end of the keys) evaluate the mask.
@@ -48,12 +52,16 @@ constexpr int kBr = 32 * kWaves;   // query rows per workgroup
 constexpr int kBc = 64;            // keys per step
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kSumLimit = 65536.0f;
-// Issue the score product of the next tile before the softmax of the current
-// one (more registers, fewer waves per SIMD) or not (more waves per SIMD hide
-// the latency instead).  Measured on MI355X: head size 128 gains from the
-// pipeline at 2 waves per SIMD; head size 64 runs faster unpipelined at 3.
-template <int D>
-constexpr bool fwd_pipelined() { return D == 128; }
+// Loop form per instantiation (measured on MI355X):
+//  0  one tile per step: scores, softmax and P V of tile t (D = 64: the
+//     plain loop at 3 waves per SIMD beats the pipelined forms at 2);
+//  1  K one tile ahead of V: the score product of tile t+1 is issued before
+//     the softmax of tile t, then tile t's P V (D = 128 without mask);
+//  2  deferred P V: step t runs S(t+1) and P V of tile t-1 on the matrix
+//     cores, interleaved product by product with the softmax of tile t on the
+//     vector unit (D = 128 causal; without the mask this form spills).
+template <int D, bool CAUSAL>
+constexpr int fwd_mode() { return D == 64 ? 0 : (CAUSAL ? 2 : 1); }
 
 struct FwdArgs {
   const __bf16* q;
@@ -66,14 +74,16 @@ struct FwdArgs {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, fwd_pipelined<D>() ? 2 : 3) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, (fwd_mode<D, CAUSAL>() == 0 ? 3 : 2)) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int KS = D / 16;           // k-steps of the score product
   constexpr int DT = D / 32;           // 32-wide output tiles
   constexpr int RB = D * 2;            // bytes per LDS row (dense, chunks swizzled)
   constexpr int TILE = kBc * RB;       // bytes of one K or V tile
   constexpr int CPW = TILE / 1024 / kWaves;   // 1 KB global->LDS copies per wave per tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];   // K0 K1 V0 V1
+  constexpr int MODE = fwd_mode<D, CAUSAL>();
+  constexpr int NV = MODE == 2 ? 3 : 2;   // V buffers
+  __shared__ __attribute__((aligned(1024))) char smem[(2 + NV) * TILE];   // K0 K1 V0 V1 [V2]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -123,11 +133,13 @@ __global__ __launch_bounds__(256, fwd_pipelined<D>() ? 2 : 3) void fwd_bf16_kern
   // are copied into the other buffers.
   char* const kbuf = smem;
   char* const vbuf = smem + 2 * TILE;
+  // Byte offset of this wave's first 1 KB block, as a wave-uniform (scalar) value.
+  const int wblk = __builtin_amdgcn_readfirstlane(wave * 1024);
   auto stage_rows = [&](const __bf16* src, int kt, char* dst) {
     const int rows = min(N - kt * kBc, kBc);
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src + (int64_t)kt * kBc * rs, (uint32_t)(rows * rs * 2));
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, svoff[i], dst + (wave + kWaves * i) * 1024);
+    for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, svoff[i], dst + wblk + kWaves * i * 1024);
   };
 
   // Lane bases of the fragment reads.  The chunk field of an address (bits
@@ -196,16 +208,16 @@ __global__ __launch_bounds__(256, fwd_pipelined<D>() ? 2 : 3) void fwd_bf16_kern
     return lsum[0] + lsum[1];
   };
 
-  // Softmax update and O^T += V^T P^T for one step.
+  // Softmax update for one step: P (bf16 operands) of the step's scores.
   //  MASK steps (diagonal or ragged end) hide keys and move the reference to
   //  the exact running max when it grows by more than 2^8.
   //  Other steps exponentiate against the current reference straight away and
   //  only look at the row max (and redo the step) if some row's share of the
   //  sum exceeds 2^16, which bounds every probability by 2^16; the reference
   //  is -inf before the first step, so the first step always takes that path.
-  auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[2], const char* vb, int k0) {
+  //  A move of the reference rescales the output accumulated so far.
+  auto softmax_tile = [&](auto mask_tag, f32x16 (&s)[2], int k0, bf16x8 (&pb)[2][2]) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    bf16x8 pb[2][2];
     float lsum;
     if constexpr (MASK) {
 #pragma unroll
@@ -233,20 +245,68 @@ __global__ __launch_bounds__(256, fwd_pipelined<D>() ? 2 : 3) void fwd_bf16_kern
       }
     }
     l_part += lsum;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          const uint32_t rowoff = (32 * j + 16 * u) * RB;
-          const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_read_tr16(vb, (vl ^ (64 * t)) + rowoff));
-          const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_read_tr16(vb, (vl ^ (64 * t + 32)) + rowoff + 8 * RB));
-          bf16x8 va;
-          va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
-          va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
-          oacc[t] = mfma32x32x16(va, pb[j][u], oacc[t]);
-        }
+  };
+
+  // O^T += V^T P^T for one step, in four groups g = (j, u) of DT products;
+  // with D = 64 the V^T reads of group g+1 are in flight while group g's
+  // products issue.
+  auto pv_tile = [&](const char* vb, const bf16x8 (&pb)[2][2]) {
+    const uint32_t vbase = lds_addr(vb);
+    s16x4 rd[4][DT][2];
+    auto issue = [&](auto G) {
+      constexpr int g = decltype(G)::value;
+      constexpr uint32_t rowoff = (uint32_t)(16 * g * RB);
+      static_for<0, DT>([&](auto T) {
+        constexpr int t = decltype(T)::value;
+        rd[g][t][0] = lds_tr16_issue<rowoff>(vbase + (vl ^ (64 * t)));
+        rd[g][t][1] = lds_tr16_issue<rowoff + 8 * RB>(vbase + (vl ^ (64 * t + 32)));
+      });
+    };
+    auto consume = [&](auto G) {
+      constexpr int g = decltype(G)::value;
+      static_for<0, DT>([&](auto T) {
+        constexpr int t = decltype(T)::value;
+        oacc[t] = mfma32x32x16(tr_pair_take(rd[g][t]), pb[g >> 1][g & 1], oacc[t]);
+      });
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    if constexpr (D == 64) {
+      issue(I0{});
+      issue(I1{});
+      lds_wait<2 * DT>();
+      consume(I0{});
+      issue(I2{});
+      lds_wait<2 * DT>();
+      consume(I1{});
+      issue(I3{});
+      lds_wait<2 * DT>();
+      consume(I2{});
+      lds_wait<0>();
+      consume(I3{});
+    } else {
+      // d = 128: one group in flight (registers are the limit here).
+      issue(I0{});
+      lds_wait<0>();
+      consume(I0{});
+      issue(I1{});
+      lds_wait<0>();
+      consume(I1{});
+      issue(I2{});
+      lds_wait<0>();
+      consume(I2{});
+      issue(I3{});
+      lds_wait<0>();
+      consume(I3{});
+    }
+  };
+
+  auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[2], const char* vb, int k0) {
+    bf16x8 pb[2][2];
+    softmax_tile(mask_tag, s, k0, pb);
+    pv_tile(vb, pb);
   };
 
   // S^T = K Q^T for the two 32-key sub-tiles of a K buffer (independent
@@ -264,7 +324,7 @@ __global__ __launch_bounds__(256, fwd_pipelined<D>() ? 2 : 3) void fwd_bf16_kern
   // Software pipeline: the score product of tile t+1 is issued before the
   // softmax of tile t, so the matrix cores work on it while the vector unit
   // exponentiates; tile t's P V product follows.
-  if constexpr (fwd_pipelined<D>()) {
+  if constexpr (MODE == 1) {
     // One step: copies for later tiles, next tile's scores into `snext`, then
     // softmax and P V of tile kt from `scur`.
     auto step = [&](int kt, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
@@ -299,6 +359,117 @@ __global__ __launch_bounds__(256, fwd_pipelined<D>() ? 2 : 3) void fwd_bf16_kern
       step(kt + 1, sb, sa);
     }
     if (kt < nkt) step(kt, sa, sb);
+  } else if constexpr (MODE == 2) {
+    // Step t: copies of K(t+2) and V(t+1); score product S(t+1) and P V of
+    // tile t-1 on the matrix cores; softmax of tile t (whose scores step t-1
+    // produced) on the vector unit.  Neither product depends on that softmax,
+    // so the two units overlap within the wave.  A move of the reference in
+    // step t rescales O after tile t-1's P V has been added, so O sees the
+    // same sequence of updates as with an immediate P V.  V has three buffers:
+    // V(t-1) is read while V(t) waits and V(t+1) is being copied.
+    // This wave's last key tile (causal: keys past its rows are skipped).
+    const int nlast = CAUSAL ? min(nkt - 1, (qw0 + 31) / kBc) : nkt - 1;
+    stage_rows(Kg, 0, kbuf);
+    stage_rows(Vg, 0, vbuf);
+    if (nkt > 1) stage_rows(Kg, 1, kbuf + TILE);
+    wait_vmem();
+    __syncthreads();
+    // One step; `sc` holds S(t), `sn` receives S(t+1), `pin` holds P(t-1) and
+    // `pout` receives P(t) (two register sets, swapped every step).
+    auto step = [&](int kt, f32x16 (&sc)[2], f32x16 (&sn)[2], const bf16x8 (&pin)[2][2],
+                    bf16x8 (&pout)[2][2]) {
+      wait_vmem();
+      __syncthreads();
+      if (kt + 2 < nkt) stage_rows(Kg, kt + 2, kbuf + (kt & 1) * TILE);
+      if (kt + 1 < nkt) stage_rows(Vg, kt + 1, vbuf + ((kt + 1) % 3) * TILE);
+      const int k0 = kt * kBc;
+      const bool do_pv = kt >= 1 && kt - 1 <= nlast;
+      const bool do_sm = kt <= nlast;
+      const bool do_s = kt + 1 <= nlast;
+      const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
+      const char* vprev = vbuf + ((kt + 2) % 3) * TILE;
+      const char* knext = kbuf + ((kt + 1) & 1) * TILE;
+      if (do_pv && do_s && do_sm && !masked) {
+        // Common case: NM slots, each one matrix product (P V of tile t-1 on
+        // even slots, S(t+1) on odd ones) followed by the softmax arithmetic
+        // of 32 / NM scores of tile t; LDS operands are read three slots ahead.
+        constexpr int NPV = 4 * DT, NM = 2 * NPV, EPS = 32 / NM;
+        static_assert(2 * KS == NPV, "as many S products as P V products");
+        const uint32_t vbase = lds_addr(vprev), kbase = lds_addr(knext);
+        constexpr int L = 3;
+        s16x4 rv[NPV][2];
+        bf16x8 rk[NPV];
+        auto issue = [&](auto I) {
+          constexpr int i = decltype(I)::value;
+          if constexpr ((i & 1) == 0) {
+            constexpr int pidx = i >> 1, g = pidx / DT, t = pidx % DT;
+            constexpr uint32_t rowoff = (uint32_t)(16 * g * RB);
+            rv[pidx][0] = lds_tr16_issue<rowoff>(vbase + (vl ^ (64 * t)));
+            rv[pidx][1] = lds_tr16_issue<rowoff + 8 * RB>(vbase + (vl ^ (64 * t + 32)));
+          } else {
+            constexpr int q = i >> 1, ks = q >> 1, j = q & 1;
+            rk[q] = lds_b128_issue<(uint32_t)(32 * j * RB)>(kbase + (kl ^ (ks << 5)));
+          }
+        };
+        static_for<0, L>([&](auto I) { issue(I); });
+        float ls[2] = {0.f, 0.f};
+        float pv[32];
+        const float nm = -m_ref;
+        static_for<0, NM>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          if constexpr (i + L < NM) issue(std::integral_constant<int, i + L>{});
+          constexpr int after = [] {
+            int n = 0;
+            for (int sl = i + 1; sl <= (i + L < NM - 1 ? i + L : NM - 1); ++sl) n += (sl & 1) ? 1 : 2;
+            return n;
+          }();
+          lds_wait<after>();
+          if constexpr ((i & 1) == 0) {
+            constexpr int pidx = i >> 1, g = pidx / DT, t = pidx % DT;
+            oacc[t] = mfma32x32x16(tr_pair_take(rv[pidx]), pin[g >> 1][g & 1], oacc[t]);
+          } else {
+            constexpr int q = i >> 1, ks = q >> 1, j = q & 1;
+            lds_ready(rk[q]);
+            sn[j] = mfma32x32x16(rk[q], qf[ks], ks == 0 ? (f32x16){} : sn[j]);
+          }
+          static_for<0, EPS>([&](auto E) {
+            constexpr int e = EPS * i + decltype(E)::value;
+            const float x = fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], c, nm));
+            pv[e] = x;
+            ls[e & 1] += x;
+          });
+          if constexpr (((i + 1) * EPS) % 8 == 0) {
+            constexpr int e0 = (i + 1) * EPS - 8, j = e0 >> 4, u = (e0 & 15) >> 3;
+            pout[j][u] = pack_bf16x8(pv[e0], pv[e0 + 1], pv[e0 + 2], pv[e0 + 3],
+                                     pv[e0 + 4], pv[e0 + 5], pv[e0 + 6], pv[e0 + 7]);
+            asm volatile("" : "+v"(pout[j][u]));   // keep the packing in this slot
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        float lsum = ls[0] + ls[1];
+        if (__any(!(lsum <= kSumLimit))) {
+          move_reference(sc);
+          lsum = exp_tile(std::false_type{}, sc, pout);
+        }
+        l_part += lsum;
+      } else {
+        if (do_pv) pv_tile(vprev, pin);
+        if (do_s) scores(knext, sn);
+        if (do_sm) {
+          if (masked) softmax_tile(std::true_type{}, sc, k0, pout);
+          else softmax_tile(std::false_type{}, sc, k0, pout);
+        }
+      }
+    };
+    f32x16 sa[2], sb[2];
+    bf16x8 pa[2][2], pb2[2][2];
+    scores(kbuf, sa);
+    int kt = 0;
+    for (; kt + 1 <= nkt; kt += 2) {
+      step(kt, sa, sb, pa, pb2);
+      step(kt + 1, sb, sa, pb2, pa);
+    }
+    if (kt <= nkt) step(kt, sa, sb, pa, pb2);
   } else {
     // Double-buffered K and V of the same tile: step t copies tile t+1 while
     // it computes scores, softmax and P V of tile t.
