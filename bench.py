@@ -72,7 +72,7 @@ def kernel_traffic(name):
     return float(m.group(1)) if cur == h.group(1) else None
 
 
-def time_forward_only(fa, torch, B, N, H, d, scale, qk_mult, seed, iters):
+def time_forward_only(fa, torch, B, N, H, d, scale, qk_mult, seed, iters, causal=True):
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     q = (torch.randn((B, N, H, d), generator=g, device="cuda", dtype=torch.float32) * qk_mult).to(torch.bfloat16)
@@ -83,19 +83,19 @@ def time_forward_only(fa, torch, B, N, H, d, scale, qk_mult, seed, iters):
     # as many untimed launches as timed ones: after the idle gap before this
     # case the clock needs a few milliseconds of load to come back up
     for _ in range(iters):
-        fa.fa_forward(q, k, v, o, lse, scale, True)
+        fa.fa_forward(q, k, v, o, lse, scale, causal)
     st = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
     ev[0].record(st)
     for i in range(iters):
-        fa.fa_forward(q, k, v, o, lse, scale, True)
+        fa.fa_forward(q, k, v, o, lse, scale, causal)
         ev[i + 1].record(st)
     torch.cuda.synchronize()
     ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
     med = ms[len(ms) // 2]
-    tf = fwd_flops(B, H, N, d, True) / (med * 1e-3) / 1e12
+    tf = fwd_flops(B, H, N, d, causal) / (med * 1e-3) / 1e12
     del q, k, v, o, lse
-    return {"shape_BNHd": [B, N, H, d], "causal": True, "median_ms": round(med, 4),
+    return {"shape_BNHd": [B, N, H, d], "causal": causal, "median_ms": round(med, 4),
             "tflops": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
 
 
@@ -258,6 +258,8 @@ def main():
         log("bench: forward-only long causal workloads")
         result["forward_only"] = {
             "c3_causal": time_forward_only(fa, torch, 4, 4096, 16, 128, synth.f32(128 ** -0.5), 1.0, 3, 20),
+            "c3_noncausal": time_forward_only(fa, torch, 4, 4096, 16, 128, synth.f32(128 ** -0.5), 1.0, 3, 20,
+                                              causal=False),
             "c4": time_forward_only(fa, torch, 1, 32768, 32, 128, synth.f32(128 ** -0.5), 2.0, 4, 10),
         }
 

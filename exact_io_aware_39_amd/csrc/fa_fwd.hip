@@ -22,11 +22,10 @@
 //    either read); every fragment address is a lane base XOR a constant.
 //  * K and V tiles live in LDS rings filled by asynchronous global -> LDS
 //    copies (no staging registers), one barrier per step.  The loop form
-//    depends on the head size and the mask (fwd_mode): one tile per step at
-//    d = 64; at d = 128 the score product of tile t+1 is issued ahead of the
-//    softmax of tile t, and with a causal mask the P V product of tile t-1 is
-//    deferred into the same step so that both products interleave with the
-//    softmax arithmetic, one product after every exp.
+//    depends on the head size and the mask (fwd_mode): one tile per step,
+//    except at d = 128 with a causal mask, where the score product of tile
+//    t+1 and the P V product of tile t-1 share step t so that both interleave
+//    with the softmax arithmetic of tile t, one product after every exp.
 //  * V^T is read with asm-issued transposing reads: the compiler would wait
 //    for every copy in flight before the builtin form of that read.
 //  * exp is exp2 with scale*log2(e) folded into one FMA.  The reference max is
@@ -53,15 +52,19 @@ constexpr int kBc = 64;            // keys per step
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kSumLimit = 65536.0f;
 // Loop form per instantiation (measured on MI355X):
-//  0  one tile per step: scores, softmax and P V of tile t (D = 64: the
-//     plain loop at 3 waves per SIMD beats the pipelined forms at 2);
+//  0  one tile per step: scores, softmax and P V of tile t (D = 64, where the
+//     plain loop at 3 waves per SIMD beats the pipelined forms at 2; and
+//     D = 128 without mask, where the other forms spill registers);
 //  1  K one tile ahead of V: the score product of tile t+1 is issued before
-//     the softmax of tile t, then tile t's P V (D = 128 without mask);
+//     the softmax of tile t, then tile t's P V (kept for comparison);
 //  2  deferred P V: step t runs S(t+1) and P V of tile t-1 on the matrix
 //     cores, interleaved product by product with the softmax of tile t on the
-//     vector unit (D = 128 causal; without the mask this form spills).
+//     vector unit (D = 128 causal).
 template <int D, bool CAUSAL>
-constexpr int fwd_mode() { return D == 64 ? 0 : (CAUSAL ? 2 : 1); }
+constexpr int fwd_mode() { return (D == 128 && CAUSAL) ? 2 : 0; }
+// Waves per SIMD the kernel is compiled for (registers: 168 or 256 VGPRs).
+template <int D>
+constexpr int fwd_waves() { return D == 64 ? 3 : 2; }
 
 struct FwdArgs {
   const __bf16* q;
@@ -74,7 +77,7 @@ struct FwdArgs {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, (fwd_mode<D, CAUSAL>() == 0 ? 3 : 2)) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int KS = D / 16;           // k-steps of the score product
   constexpr int DT = D / 32;           // 32-wide output tiles
