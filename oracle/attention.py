@@ -20,6 +20,10 @@ Sources (pages, with the part of each page followed):
   [GWL] page "Flash Attention 到底做了什么？" (guanweilu.cn), section
         "它不是一个近似算法": the fused method equals the plain computation except
         for floating-point rounding order, so the plain computation is the oracle.
+  [FAN] part "⚠️ 注意": in decode each step has a single query token against
+        the KV cache, and the variant for that case is FlashDecoding; part
+        "三招" item 2 (online softmax): partial softmax results over disjoint
+        key blocks combine by rescaling with exp(m_part - m_total).
 
 Readings taken where the pages are silent or garbled:
   * The saved statistics are the natural-log logsumexp LSE_i = m_i + ln(l_i) per
@@ -31,6 +35,12 @@ Readings taken where the pages are silent or garbled:
     dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
   * A row whose keys are all masked has no softmax; it is defined as O = 0 and
     LSE = -inf (this cannot happen for square causal attention).
+  * Decode: the nq query rows are the last nq positions of a sequence of nk
+    keys, so under the causal mask row i sees keys 0 .. nk - nq + i.  The pages
+    give no more detail of FlashDecoding than its name; the reading taken is
+    the plainest one that the online softmax supports: the keys are split into
+    chunks, each chunk gives a normalised partial output and its LSE, and the
+    partials combine as LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
 """
 from __future__ import annotations
 
@@ -38,7 +48,7 @@ import numpy as np
 
 __all__ = [
     "scores", "softmax_rows", "forward", "forward_rows", "backward",
-    "forward_bnhd", "backward_bnhd",
+    "forward_bnhd", "backward_bnhd", "decode", "merge_partials",
 ]
 
 
@@ -89,6 +99,32 @@ def forward_rows(q_rows, rows, k, v, scale, causal):
     """O and LSE for a subset of query rows (absolute indices `rows`) of one head."""
     p, _, _, lse = softmax_rows(scores(q_rows, k, scale, causal, rows=rows))
     return p @ _as64(v), lse
+
+
+def decode(q, k, v, scale, causal):
+    """Decode against a KV cache ([FAN] "⚠️ 注意"): the nq rows of q are the last
+    nq positions of the sequence of len(k) keys; O and LSE of those rows."""
+    nq, nk = np.shape(q)[0], np.shape(k)[0]
+    return forward_rows(q, np.arange(nk - nq, nk), k, v, scale, causal)
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine normalised partial results of disjoint key chunks ([FAN] "三招"
+    item 2 applied to whole chunks): LSE = log sum_s exp(LSE_s) and
+    O = sum_s exp(LSE_s - LSE) O_s.  o_parts: [S, nq, d]; lse_parts: [S, nq],
+    -inf for a chunk in which a row sees no key.  A row with no key in any chunk
+    gets O = 0 and LSE = -inf."""
+    o_parts, lse_parts = _as64(o_parts), _as64(lse_parts)
+    m = lse_parts.max(axis=0)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(lse_parts - m_safe[None, :])            # exp(-inf) = 0
+    tot = w.sum(axis=0)
+    tot_safe = np.where(empty, 1.0, tot)
+    o = (w[:, :, None] * o_parts).sum(axis=0) / tot_safe[:, None]
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m_safe + np.log(tot_safe))
+    return np.where(empty[:, None], 0.0, o), lse
 
 
 def backward(q, k, v, do, scale, causal):

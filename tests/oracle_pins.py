@@ -181,7 +181,61 @@ def pin_worked_example(ora):
     _close(lse, [m_final + math.log(l_closed)], 1e-13, "worked example LSE")
 
 
+def pin_decode(ora):
+    """Decode rows are the last rows of the full sequence: under the causal mask
+    they equal those rows of the square forward; row 0 of the decode block sees
+    exactly the keys of its prefix; without the mask the position is irrelevant;
+    one key gives O = V[0] and LSE = the single score."""
+    rng = _rng(21)
+    nk, nq, d, scale = 13, 4, 6, 0.6
+    q_full, k, v = (rng.standard_normal((nk, d)) for _ in range(3))
+    q = q_full[nk - nq:]
+    o_full, lse_full = ora.forward(q_full, k, v, scale, True)
+    o_dec, lse_dec = ora.decode(q, k, v, scale, True)
+    _close(o_dec, o_full[nk - nq:], 1e-14, "causal decode O vs last rows of the forward")
+    _close(lse_dec, lse_full[nk - nq:], 1e-14, "causal decode LSE vs last rows of the forward")
+    o_p, lse_p = ora.forward(q[:1], k[:nk - nq + 1], v[:nk - nq + 1], scale, False)
+    _close(o_dec[0], o_p[0], 1e-13, "first decode row vs unmasked prefix")
+    _close(lse_dec[0], lse_p[0], 1e-13, "first decode row LSE vs unmasked prefix")
+    o_nc, lse_nc = ora.decode(q, k, v, scale, False)
+    o_f, lse_f = ora.forward(q, k, v, scale, False)
+    _close(o_nc, o_f, 1e-14, "unmasked decode O")
+    _close(lse_nc, lse_f, 1e-14, "unmasked decode LSE")
+    o1, lse1 = ora.decode(q[:1], k[:1], v[:1], scale, True)
+    _close(o1[0], v[0], 1e-15, "single key O")
+    _close(lse1, [scale * float(q[0] @ k[0])], 1e-14, "single key LSE")
+
+
+def pin_merge(ora):
+    """Partial results of key chunks merge to the whole-row result (the online
+    softmax applied to chunks), whatever the chunking and order, including
+    chunks in which some rows see no key; two chunks with equal LSE average
+    their outputs and add ln 2 to the LSE."""
+    rng = _rng(22)
+    nk, nq, d, scale = 17, 5, 4, 0.8
+    q, k, v = rng.standard_normal((nq, d)), rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    rows = np.arange(nk - nq, nk)
+    s = ora.scores(q, k, scale, True, rows=rows)
+    o_ref, lse_ref = ora.decode(q, k, v, scale, True)
+    for cuts in ([0, 5, 6, 17], [0, 17], [0, 1, 2, 9, 13, 14, 17]):
+        parts = [(a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+        o_p, lse_p = [], []
+        for a, b in parts:
+            p_c, _, _, lse_c = ora.softmax_rows(s[:, a:b])
+            o_p.append(p_c @ v[a:b])
+            lse_p.append(lse_c)
+        for order in (slice(None), slice(None, None, -1)):
+            o_m, lse_m = ora.merge_partials(np.array(o_p)[order], np.array(lse_p)[order])
+            _close(o_m, o_ref, 1e-13, f"merged O, chunks {cuts}")
+            _close(lse_m, lse_ref, 1e-13, f"merged LSE, chunks {cuts}")
+    o_a, o_b = rng.standard_normal((1, d)), rng.standard_normal((1, d))
+    o_m, lse_m = ora.merge_partials(np.array([o_a, o_b]), np.array([[0.3], [0.3]]))
+    _close(o_m, (o_a + o_b) / 2, 1e-15, "equal-weight merge O")
+    _close(lse_m, [0.3 + math.log(2.0)], 1e-15, "equal-weight merge LSE")
+
+
 ALL_PINS = [
     pin_zero_query, pin_unit_values, pin_permutation, pin_dominant_logit, pin_causal_rows,
     pin_scipy, pin_finite_differences, pin_backward_invariants, pin_worked_example,
+    pin_decode, pin_merge,
 ]

@@ -66,6 +66,21 @@ def _backward_variant(kind):
     return backward
 
 
+def _decode_aligned_to_start(q, k, v, scale, causal):
+    return ora.forward_rows(q, np.arange(np.shape(q)[0]), k, v, scale, causal)
+
+
+def _merge_unweighted(o_parts, lse_parts):
+    o, lse = _orig_merge(o_parts, lse_parts)
+    return np.asarray(o_parts, float).mean(axis=0), lse
+
+
+def _merge_lse_max(o_parts, lse_parts):
+    o, lse = _orig_merge(o_parts, lse_parts)
+    return o, np.asarray(lse_parts, float).max(axis=0)
+
+
+_orig_merge = ora.merge_partials
 _orig_scores = ora.scores
 _orig_softmax = ora.softmax_rows
 
@@ -82,6 +97,9 @@ MUTANTS = {
     "backward_dq_without_scale": ("backward", _backward_variant("dq_noscale")),
     "backward_dk_untransposed": ("backward", _backward_variant("dk_untransposed")),
     "backward_dv_untransposed": ("backward", _backward_variant("dv_untransposed")),
+    "decode_aligned_to_start": ("decode", _decode_aligned_to_start),
+    "merge_unweighted": ("merge_partials", _merge_unweighted),
+    "merge_lse_is_max": ("merge_partials", _merge_lse_max),
 }
 
 
