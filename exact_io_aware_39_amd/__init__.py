@@ -2,6 +2,7 @@
 
     o, lse = forward(q, k, v, scale=None, causal=False)
     dq, dk, dv = backward(q, k, v, o, do, lse, scale=None, causal=False)
+    o, lse = decode(q, k, v, scale=None, causal=False, splits=0)   # q: [B, Nq, H, d], Nq <= 32
 
 Tensors are contiguous [B, N, H, d] bf16 (or fp32) CUDA tensors with d in
 {64, 128}; lse is fp32 [B, H, N].  scale defaults to d**-0.5, as in the PyTorch
@@ -15,7 +16,8 @@ import torch
 
 from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_dkdv, fa_backward_dq,  # noqa: F401
                    fa_backward_dqdkdv,
-                   fa_backward_preprocess, fa_backward_workspace_bytes, fa_forward,
+                   fa_backward_preprocess, fa_backward_workspace_bytes, fa_decode,
+                   fa_decode_splits, fa_decode_workspace_bytes, fa_forward,
                    fa_status_string, load)
 
 
@@ -39,3 +41,17 @@ def backward(q, k, v, o, do, lse, scale=None, causal=False, stream=None):
     ws = torch.empty(fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device=q.device)
     fa_backward(q, k, v, o, do, lse, dq, dk, dv, ws, _scale(q, scale), causal, stream)
     return dq, dk, dv
+
+
+def decode(q, k, v, scale=None, causal=False, splits=0, stream=None):
+    """O and LSE of a few query rows ([B, Nq, H, d]) against K/V ([B, Nk, H, d]);
+    with causal=True the rows are the last Nq positions of the sequence.
+    Allocates the outputs and the split workspace."""
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(1, fa_decode_workspace_bytes(B, H, Nq, Nk, d, splits) // 4),
+                     dtype=torch.float32, device=q.device)
+    fa_decode(q, k, v, o, lse, ws, _scale(q, scale), causal, splits, stream)
+    return o, lse

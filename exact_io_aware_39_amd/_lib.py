@@ -51,6 +51,12 @@ def load() -> ctypes.CDLL:
         fn.restype = I
     lib.fa_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.fa_backward_workspace_bytes.restype = S
+    lib.fa_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.fa_decode.restype = I
+    lib.fa_decode_splits.argtypes = [I, I, I, I, I]
+    lib.fa_decode_splits.restype = I
+    lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.fa_decode_workspace_bytes.restype = S
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -123,7 +129,7 @@ def _check_ws(workspace, B, H, N, d):
 
 
 def fa_backward_preprocess(o, do, lse, workspace, stream=None):
-    """fa_backward_preprocess: workspace = [D = rowsum(dO * O) | -LSE log2(e)] (bf16 tensors)."""
+    """fa_backward_preprocess: workspace = [-D = -rowsum(dO * O) | -LSE log2(e)] (bf16 tensors)."""
     B, N, H, d = _shape(o)
     _check((o, do), torch.bfloat16)
     _check((lse, workspace), torch.float32)
@@ -163,3 +169,26 @@ def fa_backward_dq(q, k, v, do, workspace, dq, scale: float, causal: bool, strea
     _call("fa_backward_dq", load().fa_backward_dq(
         _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace), _ptr(dq),
         B, H, N, d, float(scale), int(bool(causal)), _stream(stream)))
+
+
+def fa_decode_splits(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load().fa_decode_splits(B, H, Nq, Nk, d))
+
+
+def fa_decode_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int, splits: int = 0) -> int:
+    return int(load().fa_decode_workspace_bytes(B, H, Nq, Nk, d, splits))
+
+
+def fa_decode(q, k, v, o, lse, workspace, scale: float, causal: bool, splits: int = 0, stream=None):
+    """fa_decode: q, o [B, Nq, H, d] and k, v [B, Nk, H, d] bf16; lse [B, H, Nq] fp32."""
+    B, Nq, H, d = _shape(q)
+    Bk, Nk, Hk, dk = _shape(k)
+    if (Bk, Hk, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("fa_decode: q/o and k/v must share B, H and d, k and v the same shape")
+    _check((q, k, v, o), torch.bfloat16)
+    _check((lse, workspace), torch.float32)
+    if workspace.numel() * 4 < fa_decode_workspace_bytes(B, H, Nq, Nk, d, splits):
+        raise ValueError("workspace smaller than fa_decode_workspace_bytes()")
+    _call("fa_decode", load().fa_decode(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), B, H, Nq, Nk, d,
+        float(scale), int(bool(causal)), int(splits), _stream(stream)))

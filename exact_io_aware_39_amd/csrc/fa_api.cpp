@@ -46,6 +46,18 @@ fa_status check_tensors(std::initializer_list<const void*> tensors, std::initial
 
 fa_status to_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
+// Decode checks: the shared limits with N = Nk, then the query rows and chunks.
+fa_status check_decode(int B, int H, int Nq, int Nk, int d, float scale, int causal, int splits) {
+  fa_status st = check_common(B, H, Nk, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (Nq <= 0 || splits < 0) return FA_ERR_INVALID_ARG;
+  if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
+  if (Nq > 32 || splits > fa::kDecodeMaxSplits) return FA_ERR_UNSUPPORTED;
+  const int64_t S = splits ? splits : fa::decode_splits(B, H, Nq, Nk);
+  if ((int64_t)B * H * S > INT_MAX) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +143,29 @@ fa_status fa_backward_f32(const float* Q, const float* K, const float* V, const 
   const fa::AttnShape s{B, H, N, d, scale, causal};
   return to_status(fa::launch_bwd_f32(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, s,
                                       static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                    float* workspace, int B, int H, int Nq, int Nk, int d, float scale,
+                    int causal, int splits, void* stream) {
+  fa_status st = check_decode(B, H, Nq, Nk, d, scale, causal, splits);
+  if (st == FA_OK) st = check_tensors({Q, K, V, O}, {LSE, workspace});
+  if (st != FA_OK) return st;
+  const int S = splits ? splits : fa::decode_splits(B, H, Nq, Nk);
+  const fa::DecodeShape s{B, H, Nq, Nk, d, scale, causal, S};
+  return to_status(fa::launch_decode_bf16(Q, K, V, O, LSE, workspace, s,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int fa_decode_splits(int B, int H, int Nq, int Nk, int d) {
+  if (check_decode(B, H, Nq, Nk, d, 1.f, 0, 0) != FA_OK) return 0;
+  return fa::decode_splits(B, H, Nq, Nk);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int splits) {
+  if (check_decode(B, H, Nq, Nk, d, 1.f, 0, splits) != FA_OK) return 0;
+  const size_t S = splits ? (size_t)splits : (size_t)fa::decode_splits(B, H, Nq, Nk);
+  return (size_t)B * H * S * Nq * (d + 1) * sizeof(float);
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {

@@ -31,6 +31,19 @@ hipError_t launch_bwd_dqdkdv_bf16(const void* q, const void* k, const void* v, c
                                   hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout,
                               const float* ws, void* dq, const AttnShape& s, hipStream_t stream);
+// Decode: Nq query rows per head against Nk keys, `splits` key chunks.
+constexpr int kDecodeMaxSplits = 4096;
+struct DecodeShape {
+  int B, H, Nq, Nk, d;
+  float scale;
+  int causal;
+  int splits;
+};
+// Number of key chunks chosen when the caller passes splits = 0.
+int decode_splits(int B, int H, int Nq, int Nk);
+hipError_t launch_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                              float* ws, const DecodeShape& s, hipStream_t stream);
+
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                           const float* dout, const float* lse, float* dq, float* dk, float* dv,
                           float* dvec, const AttnShape& s, hipStream_t stream);

@@ -89,7 +89,7 @@ fa_status fa_forward_f32(const float* Q, const float* K, const float* V, float* 
  * of softmax: dV = P^T dO, dP = dO V^T, D_i = rowsum(dO * O)_i,
  * dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
  * `workspace` is caller-owned device memory of fa_backward_workspace_bytes()
- * bytes; on return its first B*H*N floats hold D ([B, H, N] fp32).
+ * bytes; on return its first B*H*N floats hold -D ([B, H, N] fp32).
  */
 fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                       const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
@@ -122,7 +122,8 @@ fa_status fa_backward_dq(const void* Q, const void* K, const void* V, const void
                          const float* workspace, void* dQ,
                          int B, int H, int N, int d, float scale, int causal, void* stream);
 
-/* Backward, float32 tensors: same contract as fa_backward, every tensor fp32. */
+/* Backward, float32 tensors: same contract as fa_backward, every tensor fp32,
+   except that on return the first B*H*N floats of the workspace hold +D. */
 fa_status fa_backward_f32(const float* Q, const float* K, const float* V, const float* O,
                           const float* dO, const float* LSE, float* dQ, float* dK, float* dV,
                           float* workspace, int B, int H, int N, int d, float scale, int causal,
@@ -130,6 +131,45 @@ fa_status fa_backward_f32(const float* Q, const float* K, const float* V, const 
 
 /* Bytes of workspace fa_backward / fa_backward_f32 need: 8 B H N (0 for invalid sizes). */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Decode against a K/V cache, bfloat16 tensors (fp32 accumulation).
+ * Page "FlashAttention" (vagrantpi.github.io PKM note), part "⚠️ 注意": in
+ * decode each step has a single query token, there is no N x N matrix and
+ * the cost is reading K and V; the variant for that case is FlashDecoding.
+ * Here the keys of each (batch, head) are split into `splits` contiguous
+ * chunks processed in parallel; each chunk yields a normalised partial output
+ * O_s and its logsumexp LSE_s (the online softmax of the page's technique 2
+ * over the chunk), kept in `workspace`, and a second launch on the same
+ * stream combines them:  LSE = log sum_s exp(LSE_s),
+ *                        O = sum_s exp(LSE_s - LSE) O_s.
+ *
+ * Q, O: [B, Nq, H, d] bf16; K, V: [B, Nk, H, d] bf16 (the row layout of the
+ * other entry points with N replaced by Nq or Nk); LSE: [B, H, Nq] fp32.
+ * causal = 0: every query row sees all Nk keys.  causal = 1: query row i is
+ * position Nk - Nq + i of the sequence and sees keys 0 .. Nk - Nq + i
+ * (requires Nq <= Nk; Nq = Nk is the square causal forward).
+ * splits: 1 .. 4096 key chunks (each holds a whole number of 32-key blocks;
+ * chunks past the last key are empty and contribute nothing), or 0 for the
+ * library's choice (fa_decode_splits).
+ * workspace: caller-owned device memory of fa_decode_workspace_bytes() bytes
+ * (4-byte aligned); its contents on return are unspecified.
+ * Limits: 1 <= Nq <= 32; Nk as N in the shared limits; d 64 or 128;
+ * B*H*chunks <= 2^31 - 1.
+ * Errors as for the other entry points, and FA_ERR_INVALID_ARG for Nq <= 0,
+ * splits < 0 or (causal = 1 and Nq > Nk); FA_ERR_UNSUPPORTED for Nq > 32 or
+ * splits > 4096.
+ */
+fa_status fa_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                    float* workspace, int B, int H, int Nq, int Nk, int d, float scale,
+                    int causal, int splits, void* stream);
+
+/* Number of key chunks fa_decode uses when called with splits = 0 (0 for invalid sizes). */
+int fa_decode_splits(int B, int H, int Nq, int Nk, int d);
+
+/* Bytes of workspace fa_decode needs: 4 B H S Nq (d + 1) with S the number of
+   chunks (splits, or fa_decode_splits() for splits = 0); 0 for invalid sizes. */
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int splits);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);

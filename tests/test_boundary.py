@@ -48,6 +48,12 @@ def lib():
     lib.fa_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_decode.argtypes = [vp] * 6 + [i] * 5 + [f, i, i, vp]
+    lib.fa_decode.restype = i
+    lib.fa_decode_splits.argtypes = [i] * 5
+    lib.fa_decode_splits.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i] * 6
+    lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -55,7 +61,8 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_f32",
         "fa_backward_preprocess", "fa_backward_dqdkdv", "fa_backward_dkdv", "fa_backward_dq",
-        "fa_backward_workspace_bytes", "fa_status_string"])
+        "fa_backward_workspace_bytes", "fa_status_string",
+        "fa_decode", "fa_decode_splits", "fa_decode_workspace_bytes"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -148,6 +155,44 @@ def test_workspace_bytes(lib):
     assert lib.fa_backward_workspace_bytes(1, 1, 1, 128) == 8
     assert lib.fa_backward_workspace_bytes(0, 16, 8192, 64) == 0
     assert lib.fa_backward_workspace_bytes(2, 16, 8192, 96) == 0
+
+
+def _dec(lib, B=1, H=2, Nq=1, Nk=100, d=64, scale=0.1, causal=1, splits=0, ptrs=(P,) * 6):
+    return lib.fa_decode(*ptrs, B, H, Nq, Nk, d, scale, causal, splits, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert _dec(lib, d=96) == UNSUPPORTED
+    assert _dec(lib, Nq=0) == INVALID
+    assert _dec(lib, Nq=33) == UNSUPPORTED
+    assert _dec(lib, Nq=5, Nk=4, causal=1) == INVALID       # more rows than keys under the mask
+    assert _dec(lib, splits=-1) == INVALID
+    assert _dec(lib, splits=4097) == UNSUPPORTED
+    assert _dec(lib, Nk=0) == INVALID
+    assert _dec(lib, Nk=(1 << 20) + 1) == UNSUPPORTED
+    assert _dec(lib, scale=float("inf")) == INVALID
+    assert _dec(lib, scale=-1.0) == UNSUPPORTED
+    assert _dec(lib, causal=2) == INVALID
+    for i in range(6):
+        ptrs = [P] * 6
+        ptrs[i] = None
+        assert _dec(lib, ptrs=tuple(ptrs)) == INVALID
+    for i in range(6):                       # Q K V O: 16-byte alignment; LSE, workspace: 4-byte
+        ptrs = [P] * 6
+        ptrs[i] = P + (2 if i >= 4 else 8)
+        assert _dec(lib, ptrs=tuple(ptrs)) == INVALID
+
+
+def test_decode_splits_and_workspace(lib):
+    # about 1024 workgroups in all, at least 8 blocks of 32 keys a chunk
+    assert lib.fa_decode_splits(8, 32, 1, 16384, 128) == 4
+    assert lib.fa_decode_splits(1, 1, 1, 31, 64) == 1
+    assert lib.fa_decode_splits(1, 1, 4, 1 << 20, 64) == 1024
+    assert lib.fa_decode_splits(1, 1, 33, 100, 64) == 0
+    assert lib.fa_decode_workspace_bytes(8, 32, 1, 16384, 128, 0) == 8 * 32 * 4 * 1 * 129 * 4
+    assert lib.fa_decode_workspace_bytes(2, 3, 5, 1000, 64, 7) == 2 * 3 * 7 * 5 * 65 * 4
+    assert lib.fa_decode_workspace_bytes(2, 3, 5, 1000, 64, 4097) == 0
+    assert lib.fa_decode_workspace_bytes(2, 3, 0, 1000, 64, 1) == 0
 
 
 def test_status_strings(lib):
