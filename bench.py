@@ -99,6 +99,41 @@ def time_forward_only(fa, torch, B, N, H, d, scale, qk_mult, seed, iters, causal
             "tflops": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
 
 
+def time_decode(fa, torch, B, Nq, Nk, H, d, seed, iters):
+    """Split-key decode of Nq rows against a [B, Nk, H, d] K/V cache (causal, the
+    rows being the last Nq positions): median launch pair (split + merge) time and
+    the HBM roofline of reading K and V once."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    q = torch.randn((B, Nq, H, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((B, Nk, H, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((B, Nk, H, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    splits = fa.fa_decode_splits(B, H, Nq, Nk, d)
+    ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, Nq, Nk, d, splits) // 4, dtype=torch.float32,
+                     device="cuda")
+    scale = d ** -0.5
+    for _ in range(iters):
+        fa.fa_decode(q, k, v, o, lse, ws, scale, True, splits)
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record(st)
+    for i in range(iters):
+        fa.fa_decode(q, k, v, o, lse, ws, scale, True, splits)
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+    med = ms[len(ms) // 2]
+    alg = 2.0 * B * Nk * H * d * 2 + 2.0 * B * Nq * H * d * 2 + 4.0 * B * H * Nq
+    gbs = alg / (med * 1e-3) / 1e9
+    del q, k, v, o, lse, ws
+    return {"shape_B_Nq_Nk_H_d": [B, Nq, Nk, H, d], "causal": True, "splits": splits,
+            "median_ms": round(med, 4), "algorithmic_bytes": alg,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def cpu_baseline(w, host, got, min_seconds=10.0):
     """Time the fp64 oracle (forward + backward) on whole heads of the workload,
     head after head, until at least `min_seconds` of CPU work; also compare the
@@ -261,6 +296,11 @@ def main():
             "c3_noncausal": time_forward_only(fa, torch, 4, 4096, 16, 128, synth.f32(128 ** -0.5), 1.0, 3, 20,
                                               causal=False),
             "c4": time_forward_only(fa, torch, 1, 32768, 32, 128, synth.f32(128 ** -0.5), 2.0, 4, 10),
+        }
+        log("bench: split-key decode against a long K/V cache")
+        result["decode"] = {
+            "nq1": time_decode(fa, torch, 8, 1, 32768, 32, 128, 6, 20),
+            "nq4": time_decode(fa, torch, 8, 4, 32768, 32, 128, 6, 20),
         }
 
     if not args.no_cpu_baseline:
