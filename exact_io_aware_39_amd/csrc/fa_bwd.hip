@@ -27,11 +27,10 @@
 //                 one scalar per lane, and dS^T feeds dQ^T += K^T dS^T directly.
 // fa_backward runs 2 and 3 as one grid (bwd_fused) ordered heaviest first, so
 // the two passes share one tail; the split entry points launch them apart.
-// Both passes stage their streamed tiles with buffer -> LDS copies into a ring
-// of LDS slots.  A software-pipelined form of each loop (the two score-like
-// products of the next tile issued ahead of the exp / dS work of the current
-// one) is kept behind kDkdvPipeline / kDqPipeline; at head size 64 the plain
-// loops at three waves per SIMD measure faster than the pipelined ones at two.
+// Both passes stage their streamed tiles with buffer -> LDS copies into two
+// LDS slots.  At head size 64 these plain loops at three waves per SIMD
+// measured faster than software-pipelined forms (the score products of the
+// next tile issued ahead of the exp / dS work of the current one) at two.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -151,29 +150,22 @@ __device__ __forceinline__ void store_row_frags(__bf16* row, const f32x16* acc, 
 }
 
 // ------------------------------------------------------------------ dK, dV pass
-// Issue the score products of the next tile before the exp/dS work of the
-// current one (more registers, fewer waves per SIMD) or not.
-constexpr bool kDkdvPipeline = false;
-constexpr bool kDqPipeline = false;
-
 constexpr int kKeysPerWg = 128;   // 4 waves x 32 keys
 constexpr int kBq = 32;           // queries per step
 
 template <int D>
 constexpr int dkdv_lds_bytes() {
-  return ((kDkdvPipeline && D == 64) ? 3 : 2) * (2 * kBq * D * 2 + 512);
+  return 2 * (2 * kBq * D * 2 + 512);
 }
 
 // dK, dV of key tile kt of head bh (one workgroup).
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char* smem) {
-  constexpr bool PIPE = kDkdvPipeline && D == 64;
-  constexpr int NSLOT = PIPE ? 3 : 2;
   constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
   constexpr int TILE = kBq * RB;            // one Q or dO tile
   constexpr int CPW = TILE / 1024 / 4;      // 1 KB copies per wave per tile
   constexpr int SLOT = 2 * TILE + 512;      // Q, dO, then 64 floats of -LSE log2 e and of D
-  static_assert(NSLOT * SLOT == dkdv_lds_bytes<D>(), "LDS layout");
+  static_assert(2 * SLOT == dkdv_lds_bytes<D>(), "LDS layout");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -285,42 +277,17 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
     else update(std::false_type{}, slot, sacc, pacc, qi0);
   };
 
-  if constexpr (PIPE) {
-    // Step s: copies of tile s+2, score products of tile s+1 (a stale slot on
-    // the last step; the result is unused), then P, dS and dV, dK of tile s.
-    auto slot_of = [&](int s) { return smem + (s % NSLOT) * SLOT; };
-    auto step = [&](int s, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn) {
-      wait_vmem();
-      __syncthreads();
-      if (s + 2 < nsteps) stage(s + 2, slot_of(s + 2));
-      scores(slot_of(s + 1), sn, pn);
-      update_tile(slot_of(s), sc, pc, s);
-    };
-    stage(0, slot_of(0));
-    if (nsteps > 1) stage(1, slot_of(1));
+  stage(0, smem);
+  for (int s = 0; s < nsteps; ++s) {
+    char* slot = smem + (s & 1) * SLOT;
     wait_vmem();
     __syncthreads();
-    f32x16 sa, pa, sb, pb2;
-    scores(slot_of(0), sa, pa);
-    int s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-      step(s, sa, pa, sb, pb2);
-      step(s + 1, sb, pb2, sa, pa);
-    }
-    if (s < nsteps) step(s, sa, pa, sb, pb2);
-  } else {
-    stage(0, smem);
-    for (int s = 0; s < nsteps; ++s) {
-      char* slot = smem + (s & 1) * SLOT;
-      wait_vmem();
-      __syncthreads();
-      if (s + 1 < nsteps) stage(s + 1, smem + ((s + 1) & 1) * SLOT);
-      const int qi0 = qstart + s * kBq;
-      if (CAUSAL && qi0 + kBq - 1 < kw0) continue;
-      f32x16 sacc, pacc;
-      scores(slot, sacc, pacc);
-      update_tile(slot, sacc, pacc, s);
-    }
+    if (s + 1 < nsteps) stage(s + 1, smem + ((s + 1) & 1) * SLOT);
+    const int qi0 = qstart + s * kBq;
+    if (CAUSAL && qi0 + kBq - 1 < kw0) continue;
+    f32x16 sacc, pacc;
+    scores(slot, sacc, pacc);
+    update_tile(slot, sacc, pacc, s);
   }
 
   if (mykey < N) {
@@ -335,15 +302,13 @@ constexpr int kBk = 64;        // keys per step
 
 template <int D>
 constexpr int dq_lds_bytes() {
-  return 2 * (kDqPipeline ? 3 : 2) * kBk * D * 2;
+  return 2 * 2 * kBk * D * 2;
 }
 
 // dQ of query tile qtile of head bh (one workgroup).
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, char* smem) {
-  // Pipelined: three K and three V slots (step t reads tiles t and t+1 while
-  // tile t+2 is being copied); otherwise two of each.
-  constexpr int NS = kDqPipeline ? 3 : 2;
+  constexpr int NS = 2;   // K and V slots each
   constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
   constexpr int TILE = kBk * RB;
   constexpr int CPW = TILE / 1024 / 4;
@@ -427,68 +392,28 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
       for (int t = 0; t < DT; ++t) dq[t] = mfma32x32x16(tr_frag<D>(kt, tfb, t, j, u), db, dq[t]);
     }
   };
-  // dS and dQ for sub-tile j of key tile t.
-  auto update_sub = [&](int t, int j, const f32x16& sacc, const f32x16& pacc) {
-    const int k0 = t * kBk;
-    if (CAUSAL && k0 + 32 * j > qw0 + 31) return;   // these keys lie past the wave's rows
-    const bool masked = (k0 + 32 * j + 32 > N) || (CAUSAL && k0 + 32 * j + 31 > qw0);
-    if (__builtin_expect(masked, 0)) update(std::true_type{}, kslot(t), j, sacc, pacc, k0);
-    else update(std::false_type{}, kslot(t), j, sacc, pacc, k0);
-  };
 
-  if constexpr (kDqPipeline) {
-    // Software pipeline over 32-key units: the score products of the next unit
-    // (the other half of this tile, or the first half of tile t+1, which was
-    // copied one step ahead) are issued before the dS work of the current unit.
-    // Step t: copies of tile t+2, then units (t, 0) and (t, 1).  On the last
-    // step the look-ahead reads a stale slot and its result is unused.
-    auto step = [&](int t, f32x16& sa, f32x16& pa, f32x16& sb, f32x16& pb2) {
-      wait_vmem();
-      __syncthreads();
-      if (t + 2 < nkt) {
-        stage_rows(a.k, t + 2, kslot(t + 2));
-        stage_rows(a.v, t + 2, vslot(t + 2));
-      }
-      if (CAUSAL && t * kBk > qw0 + 31) return;   // this and later tiles lie past the wave's rows
-      scores(kslot(t), vslot(t), 1, sb, pb2);
-      update_sub(t, 0, sa, pa);
-      scores(kslot(t + 1), vslot(t + 1), 0, sa, pa);
-      update_sub(t, 1, sb, pb2);
-    };
-    stage_rows(a.k, 0, kslot(0));
-    stage_rows(a.v, 0, vslot(0));
-    if (nkt > 1) {
-      stage_rows(a.k, 1, kslot(1));
-      stage_rows(a.v, 1, vslot(1));
-    }
+  // Double-buffered K and V of the same tile; step t copies tile t+1 while it
+  // works through the two 32-key units of tile t.
+  stage_rows(a.k, 0, kslot(0));
+  stage_rows(a.v, 0, vslot(0));
+  for (int t = 0; t < nkt; ++t) {
     wait_vmem();
     __syncthreads();
-    f32x16 sa, pa, sb, pb2;
-    scores(kslot(0), vslot(0), 0, sa, pa);
-    for (int t = 0; t < nkt; ++t) step(t, sa, pa, sb, pb2);
-  } else {
-    // Double-buffered K and V of the same tile; step t copies tile t+1 while it
-    // works through the two 32-key units of tile t.
-    stage_rows(a.k, 0, kslot(0));
-    stage_rows(a.v, 0, vslot(0));
-    for (int t = 0; t < nkt; ++t) {
-      wait_vmem();
-      __syncthreads();
-      if (t + 1 < nkt) {
-        stage_rows(a.k, t + 1, kbuf + ((t + 1) & 1) * TILE);
-        stage_rows(a.v, t + 1, vbuf + ((t + 1) & 1) * TILE);
-      }
-      if (CAUSAL && t * kBk > qw0 + 31) continue;
+    if (t + 1 < nkt) {
+      stage_rows(a.k, t + 1, kbuf + ((t + 1) & 1) * TILE);
+      stage_rows(a.v, t + 1, vbuf + ((t + 1) & 1) * TILE);
+    }
+    if (CAUSAL && t * kBk > qw0 + 31) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        f32x16 sc, pc;
-        scores(kbuf + (t & 1) * TILE, vbuf + (t & 1) * TILE, j, sc, pc);
-        const int k0 = t * kBk;
-        if (CAUSAL && k0 + 32 * j > qw0 + 31) break;
-        const bool masked = (k0 + 32 * j + 32 > N) || (CAUSAL && k0 + 32 * j + 31 > qw0);
-        if (__builtin_expect(masked, 0)) update(std::true_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
-        else update(std::false_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
-      }
+    for (int j = 0; j < 2; ++j) {
+      f32x16 sc, pc;
+      scores(kbuf + (t & 1) * TILE, vbuf + (t & 1) * TILE, j, sc, pc);
+      const int k0 = t * kBk;
+      if (CAUSAL && k0 + 32 * j > qw0 + 31) break;
+      const bool masked = (k0 + 32 * j + 32 > N) || (CAUSAL && k0 + 32 * j + 31 > qw0);
+      if (__builtin_expect(masked, 0)) update(std::true_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
+      else update(std::false_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
     }
   }
 
@@ -498,7 +423,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 // ------------------------------------------------------------------ kernels
 template <int D, bool CAUSAL>
 constexpr int bwd_min_waves() {
-  return D == 64 ? ((kDkdvPipeline || !CAUSAL) ? 2 : 3) : 1;
+  return D == 64 ? (CAUSAL ? 3 : 2) : 1;
 }
 
 template <int D, bool CAUSAL>
@@ -510,7 +435,7 @@ __global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL>())) void bwd_dkdv_ke
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, kDqPipeline ? 2 : 3) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[dq_lds_bytes<D>()];
   int bh, qt;
   tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, true, bh, qt);

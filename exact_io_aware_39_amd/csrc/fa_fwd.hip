@@ -53,10 +53,8 @@ constexpr float kRescaleLog2 = 8.0f;
 constexpr float kSumLimit = 65536.0f;
 // Loop form per instantiation (measured on MI355X):
 //  0  one tile per step: scores, softmax and P V of tile t (D = 64, where the
-//     plain loop at 3 waves per SIMD beats the pipelined forms at 2; and
-//     D = 128 without mask, where the other forms spill registers);
-//  1  K one tile ahead of V: the score product of tile t+1 is issued before
-//     the softmax of tile t, then tile t's P V (kept for comparison);
+//     plain loop at 3 waves per SIMD beat pipelined forms at 2; and D = 128
+//     without mask, where the deferred form spills registers);
 //  2  deferred P V: step t runs S(t+1) and P V of tile t-1 on the matrix
 //     cores, interleaved product by product with the softmax of tile t on the
 //     vector unit (D = 128 causal).
@@ -327,42 +325,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
   // Software pipeline: the score product of tile t+1 is issued before the
   // softmax of tile t, so the matrix cores work on it while the vector unit
   // exponentiates; tile t's P V product follows.
-  if constexpr (MODE == 1) {
-    // One step: copies for later tiles, next tile's scores into `snext`, then
-    // softmax and P V of tile kt from `scur`.
-    auto step = [&](int kt, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
-      wait_vmem();
-      __syncthreads();
-      if (kt + 2 < nkt) stage_rows(Kg, kt + 2, kbuf + (kt & 1) * TILE);
-      if (kt + 1 < nkt) stage_rows(Vg, kt + 1, vbuf + ((kt + 1) & 1) * TILE);
-      const int k0 = kt * kBc;
-      // All keys of this step lie beyond this wave's rows: nothing left to add.
-      if (CAUSAL && k0 > qw0 + 31) return;
-      // Scores of the next tile (on the last step this reads a stale buffer and
-      // the result is never used).
-      scores(kbuf + ((kt + 1) & 1) * TILE, snext);
-      const char* vb = vbuf + (kt & 1) * TILE;
-      const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
-      if (__builtin_expect(masked, 0)) softmax_pv(std::true_type{}, scur, vb, k0);
-      else softmax_pv(std::false_type{}, scur, vb, k0);
-    };
-    // Software pipeline: the score product of tile t+1 is issued before the
-    // softmax of tile t, so the matrix cores work on it while the vector unit
-    // exponentiates; tile t's P V product follows.
-    stage_rows(Kg, 0, kbuf);
-    stage_rows(Vg, 0, vbuf);
-    if (nkt > 1) stage_rows(Kg, 1, kbuf + TILE);
-    wait_vmem();
-    __syncthreads();
-    f32x16 sa[2], sb[2];
-    scores(kbuf, sa);
-    int kt = 0;
-    for (; kt + 1 < nkt; kt += 2) {
-      step(kt, sa, sb);
-      step(kt + 1, sb, sa);
-    }
-    if (kt < nkt) step(kt, sa, sb);
-  } else if constexpr (MODE == 2) {
+  if constexpr (MODE == 2) {
     // Step t: copies of K(t+2) and V(t+1); score product S(t+1) and P V of
     // tile t-1 on the matrix cores; softmax of tile t (whose scores step t-1
     // produced) on the vector unit.  Neither product depends on that softmax,
