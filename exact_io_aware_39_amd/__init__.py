@@ -2,6 +2,7 @@
 
     o, lse = forward(q, k, v, scale=None, causal=False)
     dq, dk, dv = backward(q, k, v, o, do, lse, scale=None, causal=False)
+    o, lse = forward_cross(q, k, v, scale=None, causal=False)      # q: [B, Nq, H, d], k: [B, Nk, H, d]
     o, lse = decode(q, k, v, scale=None, causal=False, splits=0)   # q: [B, Nq, H, d], Nq <= 32
 
 Tensors are contiguous [B, N, H, d] bf16 (or fp32) CUDA tensors with d in
@@ -17,7 +18,7 @@ import torch
 from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_dkdv, fa_backward_dq,  # noqa: F401
                    fa_backward_dqdkdv,
                    fa_backward_preprocess, fa_backward_workspace_bytes, fa_decode,
-                   fa_decode_splits, fa_decode_workspace_bytes, fa_forward,
+                   fa_decode_splits, fa_decode_workspace_bytes, fa_forward, fa_forward_cross,
                    fa_status_string, load)
 
 
@@ -31,6 +32,16 @@ def forward(q, k, v, scale=None, causal=False, stream=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa_forward(q, k, v, o, lse, _scale(q, scale), causal, stream)
+    return o, lse
+
+
+def forward_cross(q, k, v, scale=None, causal=False, stream=None):
+    """O and LSE of Nq query rows against Nk keys; with causal=True the rows are
+    the last Nq positions of the sequence.  Allocates the outputs."""
+    B, Nq, H, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_forward_cross(q, k, v, o, lse, _scale(q, scale), causal, stream)
     return o, lse
 
 

@@ -51,6 +51,8 @@ def load() -> ctypes.CDLL:
         fn.restype = I
     lib.fa_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.fa_backward_workspace_bytes.restype = S
+    lib.fa_forward_cross.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
+    lib.fa_forward_cross.restype = I
     lib.fa_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.fa_decode.restype = I
     lib.fa_decode_splits.argtypes = [I, I, I, I, I]
@@ -192,3 +194,16 @@ def fa_decode(q, k, v, o, lse, workspace, scale: float, causal: bool, splits: in
     _call("fa_decode", load().fa_decode(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), B, H, Nq, Nk, d,
         float(scale), int(bool(causal)), int(splits), _stream(stream)))
+
+
+def fa_forward_cross(q, k, v, o, lse, scale: float, causal: bool, stream=None):
+    """fa_forward_cross: q, o [B, Nq, H, d] and k, v [B, Nk, H, d] bf16; lse [B, H, Nq] fp32."""
+    B, Nq, H, d = _shape(q)
+    Bk, Nk, Hk, dk = _shape(k)
+    if (Bk, Hk, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("fa_forward_cross: q/o and k/v must share B, H and d, k and v the same shape")
+    _check((q, k, v, o), torch.bfloat16)
+    _check((lse,), torch.float32)
+    _call("fa_forward_cross", load().fa_forward_cross(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+        int(bool(causal)), _stream(stream)))

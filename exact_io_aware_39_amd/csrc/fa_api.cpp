@@ -71,6 +71,18 @@ fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float
   return to_status(fa::launch_fwd_bf16(Q, K, V, O, LSE, s, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_forward_cross(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                           void* stream) {
+  fa_status st = check_common(B, H, Nq, d, scale, causal);
+  if (st == FA_OK) st = check_common(B, H, Nk, d, scale, causal);
+  if (st == FA_OK && causal && Nq > Nk) st = FA_ERR_INVALID_ARG;
+  if (st == FA_OK) st = check_tensors({Q, K, V, O}, {LSE});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, Nq, d, scale, causal};
+  return to_status(fa::launch_fwd_cross_bf16(Q, K, V, O, LSE, s, Nk, static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
                          int B, int H, int N, int d, float scale, int causal, void* stream) {
   fa_status st = check_common(B, H, N, d, scale, causal);

@@ -70,7 +70,9 @@ struct FwdArgs {
   const __bf16* v;
   __bf16* o;
   float* lse;
-  int H, N, nqt, BH;
+  int H, N, nqt, BH;   // N: query rows per head
+  int Nk;               // key rows per head
+  int qoff;             // sequence position of query row 0 (causal: Nk - N)
   float c;   // scale * log2(e)
 };
 
@@ -93,12 +95,13 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
   int bh, qt;
   tile_of(blockIdx.x, a.nqt, a.BH, CAUSAL, true, bh, qt);
   const int b = bh / a.H, h = bh - b * a.H;
-  const int N = a.N;
+  const int N = a.N, Nk = a.Nk, qoff = a.qoff;
   const int64_t rs = (int64_t)a.H * D;                       // row stride (elements)
-  const int64_t base = ((int64_t)b * N * a.H + h) * D;
+  const int64_t base = ((int64_t)b * N * a.H + h) * D;       // Q and O
+  const int64_t kvbase = ((int64_t)b * Nk * a.H + h) * D;    // K and V
   const __bf16* __restrict__ Qg = a.q + base;
-  const __bf16* __restrict__ Kg = a.k + base;
-  const __bf16* __restrict__ Vg = a.v + base;
+  const __bf16* __restrict__ Kg = a.k + kvbase;
+  const __bf16* __restrict__ Vg = a.v + kvbase;
 
   const int q0 = qt * kBr;
   const int qw0 = q0 + wave * 32;
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
       qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + hh) * 8);
   }
 
-  const int kend = CAUSAL ? min(N, q0 + kBr) : N;
+  const int kend = CAUSAL ? min(Nk, q0 + qoff + kBr) : Nk;
   const int nkt = (kend + kBc - 1) / kBc;
 
   // Staging: copy i of this wave fills LDS block (wave + 4 i) of a tile; lane
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
   // Byte offset of this wave's first 1 KB block, as a wave-uniform (scalar) value.
   const int wblk = __builtin_amdgcn_readfirstlane(wave * 1024);
   auto stage_rows = [&](const __bf16* src, int kt, char* dst) {
-    const int rows = min(N - kt * kBc, kBc);
+    const int rows = min(Nk - kt * kBc, kBc);
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src + (int64_t)kt * kBc * rs, (uint32_t)(rows * rs * 2));
 #pragma unroll
     for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, svoff[i], dst + wblk + kWaves * i * 1024);
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool hide = key >= N || (CAUSAL && key > myq);
+          const bool hide = key >= Nk || (CAUSAL && key > myq + qoff);
           s[j][r] = hide ? -INFINITY : s[j][r];
         }
       float mx = -INFINITY;
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
     // same sequence of updates as with an immediate P V.  V has three buffers:
     // V(t-1) is read while V(t) waits and V(t+1) is being copied.
     // This wave's last key tile (causal: keys past its rows are skipped).
-    const int nlast = CAUSAL ? min(nkt - 1, (qw0 + 31) / kBc) : nkt - 1;
+    const int nlast = CAUSAL ? min(nkt - 1, (qw0 + qoff + 31) / kBc) : nkt - 1;
     stage_rows(Kg, 0, kbuf);
     stage_rows(Vg, 0, vbuf);
     if (nkt > 1) stage_rows(Kg, 1, kbuf + TILE);
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
       const bool do_pv = kt >= 1 && kt - 1 <= nlast;
       const bool do_sm = kt <= nlast;
       const bool do_s = kt + 1 <= nlast;
-      const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
+      const bool masked = (k0 + kBc > Nk) || (CAUSAL && k0 + kBc - 1 > qw0 + qoff);
       const char* vprev = vbuf + ((kt + 2) % 3) * TILE;
       const char* knext = kbuf + ((kt + 1) & 1) * TILE;
       if (do_pv && do_s && do_sm && !masked) {
@@ -450,10 +453,10 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
         stage_rows(Vg, kt + 1, vbuf + (cur ^ 1) * TILE);
       }
       const int k0 = kt * kBc;
-      if (CAUSAL && k0 > qw0 + 31) continue;
+      if (CAUSAL && k0 > qw0 + qoff + 31) continue;
       f32x16 sc[2];
       scores(kbuf + cur * TILE, sc);
-      const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
+      const bool masked = (k0 + kBc > Nk) || (CAUSAL && k0 + kBc - 1 > qw0 + qoff);
       if (__builtin_expect(masked, 0)) softmax_pv(std::true_type{}, sc, vbuf + cur * TILE, k0);
       else softmax_pv(std::false_type{}, sc, vbuf + cur * TILE, k0);
     }
@@ -486,8 +489,8 @@ hipError_t launch(const FwdArgs& args, int BH, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           const AttnShape& s, hipStream_t stream) {
+hipError_t launch_fwd_cross_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const AttnShape& s, int Nk, hipStream_t stream) {
   FwdArgs a;
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
@@ -496,12 +499,19 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   a.lse = lse;
   a.H = s.H;
   a.N = s.N;
+  a.Nk = Nk;
+  a.qoff = s.causal ? Nk - s.N : 0;
   a.nqt = (s.N + kBr - 1) / kBr;
   a.BH = s.B * s.H;
   a.c = s.scale * kLog2e;
   const int BH = s.B * s.H;
   if (s.d == 64) return s.causal ? launch<64, true>(a, BH, stream) : launch<64, false>(a, BH, stream);
   return s.causal ? launch<128, true>(a, BH, stream) : launch<128, false>(a, BH, stream);
+}
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const AttnShape& s, hipStream_t stream) {
+  return launch_fwd_cross_bf16(q, k, v, o, lse, s, s.N, stream);
 }
 
 }  // namespace fa

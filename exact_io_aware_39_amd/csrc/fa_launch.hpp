@@ -16,6 +16,10 @@ struct AttnShape {
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            const AttnShape& s, hipStream_t stream);
+// Forward with N query rows against Nk key rows; with a causal mask query row
+// i is sequence position Nk - N + i.
+hipError_t launch_fwd_cross_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const AttnShape& s, int Nk, hipStream_t stream);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           const AttnShape& s, hipStream_t stream);
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,

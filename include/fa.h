@@ -75,6 +75,19 @@ fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float
                      int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
+ * Forward with Nq query rows against Nk key rows per head, bfloat16 tensors:
+ * Q and O are [B, Nq, H, d], K and V [B, Nk, H, d], LSE [B, H, Nq].
+ * causal = 0: every query row sees all Nk keys (cross-attention).
+ * causal = 1: query row i is sequence position Nk - Nq + i and sees keys
+ * 0 .. Nk - Nq + i (rows appended after a cached prefix; requires Nq <= Nk;
+ * Nq = Nk is fa_forward).  Same kernels, layouts, checks and limits as
+ * fa_forward, applied to both lengths.
+ */
+fa_status fa_forward_cross(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                           void* stream);
+
+/*
  * Forward, float32 tensors: same contract as fa_forward with every tensor
  * float32 (fp32 products and accumulation throughout).
  */
