@@ -64,6 +64,14 @@ constexpr int fwd_mode() { return (D == 128 && CAUSAL) ? 2 : 0; }
 template <int D>
 constexpr int fwd_waves() { return D == 64 ? 3 : 2; }
 
+// Buffer index carried by a step's buffer tag: the constant of a
+// compile-time tag, 0 for a run-time one (whose offset is in the pointer).
+template <class T>
+constexpr int buffer_index() {
+  if constexpr (std::is_same_v<T, int>) return 0;
+  else return T::value;
+}
+
 struct FwdArgs {
   const __bf16* q;
   const __bf16* k;
@@ -254,7 +262,8 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
   // O^T += V^T P^T for one step, in four groups g = (j, u) of DT products;
   // with D = 64 the V^T reads of group g+1 are in flight while group g's
   // products issue.
-  auto pv_tile = [&](const char* vb, const bf16x8 (&pb)[2][2]) {
+  auto pv_tile = [&](const char* vb, const bf16x8 (&pb)[2][2], auto off_tag) {
+    constexpr uint32_t BOFF = decltype(off_tag)::value;
     const uint32_t vbase = lds_addr(vb);
     s16x4 rd[4][DT][2];
     auto issue = [&](auto G) {
@@ -262,8 +271,8 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
       constexpr uint32_t rowoff = (uint32_t)(16 * g * RB);
       static_for<0, DT>([&](auto T) {
         constexpr int t = decltype(T)::value;
-        rd[g][t][0] = lds_tr16_issue<rowoff>(vbase + (vl ^ (64 * t)));
-        rd[g][t][1] = lds_tr16_issue<rowoff + 8 * RB>(vbase + (vl ^ (64 * t + 32)));
+        rd[g][t][0] = lds_tr16_issue<BOFF + rowoff>(vbase + (vl ^ (64 * t)));
+        rd[g][t][1] = lds_tr16_issue<BOFF + rowoff + 8 * RB>(vbase + (vl ^ (64 * t + 32)));
       });
     };
     auto consume = [&](auto G) {
@@ -307,10 +316,10 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
     }
   };
 
-  auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[2], const char* vb, int k0) {
+  auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[2], const char* vb, auto off_tag, int k0) {
     bf16x8 pb[2][2];
     softmax_tile(mask_tag, s, k0, pb);
-    pv_tile(vb, pb);
+    pv_tile(vb, pb, off_tag);
   };
 
   // S^T = K Q^T for the two 32-key sub-tiles of a K buffer (independent
@@ -422,7 +431,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
         }
         l_part += lsum;
       } else {
-        if (do_pv) pv_tile(vprev, pin);
+        if (do_pv) pv_tile(vprev, pin, std::integral_constant<uint32_t, 0>{});
         if (do_s) scores(knext, sn);
         if (do_sm) {
           if (masked) softmax_tile(std::true_type{}, sc, k0, pout);
@@ -444,8 +453,12 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
     // it computes scores, softmax and P V of tile t.
     stage_rows(Kg, 0, kbuf);
     stage_rows(Vg, 0, vbuf);
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int cur = kt & 1;
+    // Step kt; `cur_tag` is the buffer holding tile kt (kt & 1), a
+    // compile-time constant in the two-step loops so that the buffer's LDS
+    // offset is an immediate of every fragment read.
+    auto step = [&](int kt, auto mask_tag, auto cur_tag) {
+      constexpr bool CT = !std::is_same_v<decltype(cur_tag), int>;
+      const int cur = cur_tag;
       wait_vmem();
       __syncthreads();
       if (kt + 1 < nkt) {
@@ -453,12 +466,41 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
         stage_rows(Vg, kt + 1, vbuf + (cur ^ 1) * TILE);
       }
       const int k0 = kt * kBc;
-      if (CAUSAL && k0 > qw0 + qoff + 31) continue;
+      if (CAUSAL && k0 > qw0 + qoff + 31) return;
       f32x16 sc[2];
       scores(kbuf + cur * TILE, sc);
-      const bool masked = (k0 + kBc > Nk) || (CAUSAL && k0 + kBc - 1 > qw0 + qoff);
-      if (__builtin_expect(masked, 0)) softmax_pv(std::true_type{}, sc, vbuf + cur * TILE, k0);
-      else softmax_pv(std::false_type{}, sc, vbuf + cur * TILE, k0);
+      const char* vb = CT ? vbuf : vbuf + cur * TILE;
+      using Off = std::integral_constant<uint32_t, (uint32_t)(buffer_index<decltype(cur_tag)>() * TILE)>;
+      if constexpr (decltype(mask_tag)::value) {
+        const bool masked = (k0 + kBc > Nk) || (CAUSAL && k0 + kBc - 1 > qw0 + qoff);
+        if (masked) softmax_pv(std::true_type{}, sc, vb, Off{}, k0);
+        else softmax_pv(std::false_type{}, sc, vb, Off{}, k0);
+      } else {
+        softmax_pv(std::false_type{}, sc, vb, Off{}, k0);
+      }
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    if constexpr (CAUSAL) {
+      int kt = 0;
+      for (; kt + 1 < nkt; kt += 2) {
+        step(kt, std::true_type{}, B0{});
+        step(kt + 1, std::true_type{}, B1{});
+      }
+      if (kt < nkt) step(kt, std::true_type{}, B0{});
+    } else {
+      // Without a mask only a ragged last tile hides keys, so the loop over
+      // the full tiles has a single softmax path.  With the masked path as a
+      // branch inside the loop, the compiler kept O in two register sets and
+      // copied it twice per step (a fifth of the d = 128 loop's time).
+      const int nfull = Nk / kBc;
+      int kt = 0;
+      for (; kt + 1 < nfull; kt += 2) {
+        step(kt, std::false_type{}, B0{});
+        step(kt + 1, std::false_type{}, B1{});
+      }
+      if (kt < nfull) step(kt++, std::false_type{}, B0{});
+      if (kt < nkt) step(kt, std::true_type{}, kt & 1);
     }
   }
 
