@@ -201,6 +201,12 @@ __device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rsrc, uint
 
 // Wait until this wave's global loads (including global -> LDS copies) are done.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most N global memory operations of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
 // XCD runs one contiguous range of logical tiles (neighbouring tiles share the

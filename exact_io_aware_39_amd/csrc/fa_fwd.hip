@@ -9,7 +9,7 @@
 // "知识点13 | FlashAttention深度攻略" (blog.xiaohack.org): query blocks are the
 // parallel dimension (one workgroup each) and keys are the inner loop.
 //
-// gfx950 mapping (one workgroup = 4 waves = 128 query rows; 64 keys a step):
+// gfx950 mapping (32 query rows per wave; 64 keys a step):
 //  * S^T = K Q^T is computed with v_mfma_f32_32x32x16_bf16 so that each lane
 //    of a wave owns one query row (column of S^T) and 16 of every 32 keys; the
 //    per-row softmax state lives in that lane and only the row max needs one
@@ -21,11 +21,11 @@
 //    rows are dense with XOR-permuted 16-byte chunks (no bank conflicts for
 //    either read); every fragment address is a lane base XOR a constant.
 //  * K and V tiles live in LDS rings filled by asynchronous global -> LDS
-//    copies (no staging registers), one barrier per step.  The loop form
-//    depends on the head size and the mask (fwd_mode): one tile per step,
-//    except at d = 128 with a causal mask, where the score product of tile
-//    t+1 and the P V product of tile t-1 share step t so that both interleave
-//    with the softmax arithmetic of tile t, one product after every exp.
+//    copies (no staging registers).  The loop form depends on the head size
+//    (fwd_mode): at d = 64 one workgroup of 4 waves takes one tile per step
+//    (scores, softmax, P V) with one barrier per step; at d = 128 a workgroup
+//    of 8 waves pairs the two waves of each SIMD in opposite phases, so that
+//    one runs its matrix products while the other runs its softmax.
 //  * V^T is read with asm-issued transposing reads: the compiler would wait
 //    for every copy in flight before the builtin form of that read.
 //  * exp is exp2 with scale*log2(e) folded into one FMA.  The reference max is
@@ -46,21 +46,25 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kBr = 32 * kWaves;   // query rows per workgroup
 constexpr int kBc = 64;            // keys per step
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kSumLimit = 65536.0f;
 // Loop form per instantiation (measured on MI355X):
-//  0  one tile per step: scores, softmax and P V of tile t (D = 64, where the
-//     plain loop at 3 waves per SIMD beat pipelined forms at 2; and D = 128
-//     without mask, where the deferred form spills registers);
-//  2  deferred P V: step t runs S(t+1) and P V of tile t-1 on the matrix
-//     cores, interleaved product by product with the softmax of tile t on the
-//     vector unit (D = 128 causal).
+//  0  one tile per step: scores, softmax and P V of tile t, 4 waves per
+//     workgroup at 3 waves per SIMD (D = 64: the vector work of a step
+//     exceeds its matrix work, so pairing waves by phase gains little);
+//  3  ping-pong: 8 waves, two per SIMD in opposite phases; while one wave of
+//     a SIMD runs the products of its step (S(t) and P V of tile t-1) the
+//     other runs the softmax of its tile, and barriers swap the roles
+//     (D = 128).  Waves of one SIMD that share a phase compete for the same
+//     pipe; a probe of the two arrangements measured 3400 against 2100
+//     cycles for two d = 128 steps.
 template <int D, bool CAUSAL>
-constexpr int fwd_mode() { return (D == 128 && CAUSAL) ? 2 : 0; }
-// Waves per SIMD the kernel is compiled for (registers: 168 or 256 VGPRs).
+constexpr int fwd_mode() { return D == 128 ? 3 : 0; }
+// Waves per workgroup (32 query rows each) and per SIMD (registers: 168 or
+// 256 VGPRs).
+template <int D, bool CAUSAL>
+constexpr int fwd_wg_waves() { return fwd_mode<D, CAUSAL>() == 3 ? 8 : 4; }
 template <int D>
 constexpr int fwd_waves() { return D == 64 ? 3 : 2; }
 
@@ -85,16 +89,19 @@ struct FwdArgs {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL>()), fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int KS = D / 16;           // k-steps of the score product
   constexpr int DT = D / 32;           // 32-wide output tiles
   constexpr int RB = D * 2;            // bytes per LDS row (dense, chunks swizzled)
   constexpr int TILE = kBc * RB;       // bytes of one K or V tile
-  constexpr int CPW = TILE / 1024 / kWaves;   // 1 KB global->LDS copies per wave per tile
   constexpr int MODE = fwd_mode<D, CAUSAL>();
-  constexpr int NV = MODE == 2 ? 3 : 2;   // V buffers
-  __shared__ __attribute__((aligned(1024))) char smem[(2 + NV) * TILE];   // K0 K1 V0 V1 [V2]
+  constexpr int kWaves = fwd_wg_waves<D, CAUSAL>();
+  constexpr int kBr = 32 * kWaves;     // query rows per workgroup
+  constexpr int CPW = TILE / 1024 / kWaves;   // 1 KB global->LDS copies per wave per tile
+  constexpr int NK = MODE == 3 ? 4 : 2;   // K buffers
+  constexpr int NV = NK;                  // V buffers
+  __shared__ __attribute__((aligned(1024))) char smem[(NK + NV) * TILE];   // K buffers, then V buffers
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -112,7 +119,9 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
   const __bf16* __restrict__ Vg = a.v + kvbase;
 
   const int q0 = qt * kBr;
-  const int qw0 = q0 + wave * 32;
+  // Mode 3: waves 0-3 take 32-row blocks 0, 2, 4, 6 of the tile and waves 4-7
+  // blocks 1, 3, 5, 7, so both halves reach the diagonal together.
+  const int qw0 = q0 + 32 * (MODE == 3 ? 2 * (wave & 3) + (wave >> 2) : wave);
   const int myq = qw0 + l32;
 
   // Q^T operand for this lane's row: chunk 2*ks + hh of the row, per k-step.
@@ -140,14 +149,13 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
     const int row = slot / CH;
     svoff[i] = (uint32_t)(row * rs * 2) + (uint32_t)(((slot % CH) ^ swz<D>(row)) * 16);
   }
-  // LDS: two K buffers and two V buffers.  Step t reads K of tile t+1 (for the
-  // next score product) and V of tile t, while tile t+2's K and tile t+1's V
-  // are copied into the other buffers.
+  // LDS: NK K buffers, then NV V buffers (two each for the plain loop, four
+  // for the ping-pong loop).
   char* const kbuf = smem;
-  char* const vbuf = smem + 2 * TILE;
+  char* const vbuf = smem + NK * TILE;
   // Byte offset of this wave's first 1 KB block, as a wave-uniform (scalar) value.
   const int wblk = __builtin_amdgcn_readfirstlane(wave * 1024);
-  auto stage_rows = [&](const __bf16* src, int kt, char* dst) {
+  auto stage_rows = [&](const __bf16* src, int kt, char* dst) __attribute__((always_inline)) {
     const int rows = min(Nk - kt * kBc, kBc);
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src + (int64_t)kt * kBc * rs, (uint32_t)(rows * rs * 2));
 #pragma unroll
@@ -180,7 +188,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
 
   // Moves the reference max to the exact running max of the rows (in log2
   // units) and rescales the running sum and output to it.
-  auto move_reference = [&](f32x16 (&s)[2]) {
+  auto move_reference = [&](f32x16 (&s)[2]) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
   };
 
   // P = exp2(c S - m_ref) for one step, its row-sum share, and bf16 operands.
-  auto exp_tile = [&](auto mask_tag, const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) {
+  auto exp_tile = [&](auto mask_tag, const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const float nm = -m_ref;
     float lsum[2] = {0.f, 0.f};
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
   //  sum exceeds 2^16, which bounds every probability by 2^16; the reference
   //  is -inf before the first step, so the first step always takes that path.
   //  A move of the reference rescales the output accumulated so far.
-  auto softmax_tile = [&](auto mask_tag, f32x16 (&s)[2], int k0, bf16x8 (&pb)[2][2]) {
+  auto softmax_tile = [&](auto mask_tag, f32x16 (&s)[2], int k0, bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     float lsum;
     if constexpr (MASK) {
@@ -262,11 +270,11 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
   // O^T += V^T P^T for one step, in four groups g = (j, u) of DT products;
   // with D = 64 the V^T reads of group g+1 are in flight while group g's
   // products issue.
-  auto pv_tile = [&](const char* vb, const bf16x8 (&pb)[2][2], auto off_tag) {
+  auto pv_tile = [&](const char* vb, const bf16x8 (&pb)[2][2], auto off_tag) __attribute__((always_inline)) {
     constexpr uint32_t BOFF = decltype(off_tag)::value;
     const uint32_t vbase = lds_addr(vb);
     s16x4 rd[4][DT][2];
-    auto issue = [&](auto G) {
+    auto issue = [&](auto G) __attribute__((always_inline)) {
       constexpr int g = decltype(G)::value;
       constexpr uint32_t rowoff = (uint32_t)(16 * g * RB);
       static_for<0, DT>([&](auto T) {
@@ -275,7 +283,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
         rd[g][t][1] = lds_tr16_issue<BOFF + rowoff + 8 * RB>(vbase + (vl ^ (64 * t + 32)));
       });
     };
-    auto consume = [&](auto G) {
+    auto consume = [&](auto G) __attribute__((always_inline)) {
       constexpr int g = decltype(G)::value;
       static_for<0, DT>([&](auto T) {
         constexpr int t = decltype(T)::value;
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
     }
   };
 
-  auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[2], const char* vb, auto off_tag, int k0) {
+  auto softmax_pv = [&](auto mask_tag, f32x16 (&s)[2], const char* vb, auto off_tag, int k0) __attribute__((always_inline)) {
     bf16x8 pb[2][2];
     softmax_tile(mask_tag, s, k0, pb);
     pv_tile(vb, pb, off_tag);
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
 
   // S^T = K Q^T for the two 32-key sub-tiles of a K buffer (independent
   // accumulation chains interleaved).
-  auto scores = [&](const char* kb, f32x16 (&s)[2]) {
+  auto scores = [&](const char* kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
     s[0] = (f32x16){};
     s[1] = (f32x16){};
 #pragma unroll
@@ -334,65 +342,84 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
         s[j] = mfma32x32x16(lds_read_b128(kb, (kl ^ (ks << 5)) + 32 * j * RB), qf[ks], s[j]);
   };
 
-  // Software pipeline: the score product of tile t+1 is issued before the
-  // softmax of tile t, so the matrix cores work on it while the vector unit
-  // exponentiates; tile t's P V product follows.
-  if constexpr (MODE == 2) {
-    // Step t: copies of K(t+2) and V(t+1); score product S(t+1) and P V of
-    // tile t-1 on the matrix cores; softmax of tile t (whose scores step t-1
-    // produced) on the vector unit.  Neither product depends on that softmax,
-    // so the two units overlap within the wave.  A move of the reference in
-    // step t rescales O after tile t-1's P V has been added, so O sees the
-    // same sequence of updates as with an immediate P V.  V has three buffers:
-    // V(t-1) is read while V(t) waits and V(t+1) is being copied.
-    // This wave's last key tile (causal: keys past its rows are skipped).
-    const int nlast = CAUSAL ? min(nkt - 1, (qw0 + qoff + 31) / kBc) : nkt - 1;
-    stage_rows(Kg, 0, kbuf);
-    stage_rows(Vg, 0, vbuf);
-    if (nkt > 1) stage_rows(Kg, 1, kbuf + TILE);
-    wait_vmem();
-    __syncthreads();
-    // One step; `sc` holds S(t), `sn` receives S(t+1), `pin` holds P(t-1) and
-    // `pout` receives P(t) (two register sets, swapped every step).
-    auto step = [&](int kt, f32x16 (&sc)[2], f32x16 (&sn)[2], const bf16x8 (&pin)[2][2],
-                    bf16x8 (&pout)[2][2]) {
-      wait_vmem();
-      __syncthreads();
-      if (kt + 2 < nkt) stage_rows(Kg, kt + 2, kbuf + (kt & 1) * TILE);
-      if (kt + 1 < nkt) stage_rows(Vg, kt + 1, vbuf + ((kt + 1) % 3) * TILE);
-      const int k0 = kt * kBc;
-      const bool do_pv = kt >= 1 && kt - 1 <= nlast;
-      const bool do_sm = kt <= nlast;
-      const bool do_s = kt + 1 <= nlast;
-      const bool masked = (k0 + kBc > Nk) || (CAUSAL && k0 + kBc - 1 > qw0 + qoff);
-      const char* vprev = vbuf + ((kt + 2) % 3) * TILE;
-      const char* knext = kbuf + ((kt + 1) & 1) * TILE;
-      if (do_pv && do_s && do_sm && !masked) {
-        // Common case: NM slots, each one matrix product (P V of tile t-1 on
-        // even slots, S(t+1) on odd ones) followed by the softmax arithmetic
-        // of 32 / NM scores of tile t; LDS operands are read three slots ahead.
-        constexpr int NPV = 4 * DT, NM = 2 * NPV, EPS = 32 / NM;
+  if constexpr (MODE == 3) {
+    // Ping-pong.  Global phase p ends with a workgroup barrier.  Waves 0-3
+    // (half A) run the products of step t in phase 2t and the softmax of tile
+    // t in phase 2t+1; waves 4-7 (half B; wave w and wave w+4 share a SIMD)
+    // run the same sequence one phase later.  The products of step t are
+    // S(t) = K(t) Q^T and P V of tile t-1 (the softmax of tile t-1 ran in
+    // between), so a move of the reference in softmax(t) rescales O after
+    // P V of tile t-1 has been added, as in the plain loop.  The product
+    // phases run at a raised wave priority so that the matrix pipe, not the
+    // other wave's vector work, gets the issue slots.
+    const int half = __builtin_amdgcn_readfirstlane(wave >> 2);
+    const int nlast = __builtin_amdgcn_readfirstlane(CAUSAL ? min(nkt - 1, (qw0 + qoff + 31) / kBc) : nkt - 1);
+    // Phase barriers are asm so that no release fence drains the copies in
+    // flight; the memory clobber keeps LDS accesses on their side.
+    auto phase_end = [] {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Copies run two tiles ahead through four buffers each (tile t in buffer
+    // t & 3).  Batch t (K(t+2) and V(t+1)) is issued at the end of a softmax
+    // phase, after the vector work: by half B in phase 2t, by half A in
+    // phase 2t+1.  The barrier ending phase 2t+1 leaves only each wave's
+    // latest batch in flight (s_waitcnt vmcnt(2 CPW)), so batch t-1, which
+    // the products of step t+1 read from phase 2t+2 on, is complete; the
+    // buffers batch t overwrites were last read in phase 2t-1.  Every batch
+    // is 2 CPW copies per wave: a tile past the last one is copied from an
+    // empty range (no memory is read) into a buffer nobody reads again, so
+    // the count of copies in flight is the same every phase.
+    auto stage_or_skip = [&](const __bf16* src, int kt, char* dst) __attribute__((always_inline)) {
+      const bool real = kt < nkt;
+      const int rows = real ? min(Nk - kt * kBc, kBc) : 0;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          make_rsrc(src + (int64_t)(real ? kt : 0) * kBc * rs, (uint32_t)(rows * rs * 2));
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, svoff[i], dst + wblk + kWaves * i * 1024);
+    };
+    auto copies = [&](int t) __attribute__((always_inline)) {
+      stage_or_skip(Kg, t + 2, kbuf + ((t + 2) & 3) * TILE);
+      stage_or_skip(Vg, t + 1, vbuf + ((t + 1) & 3) * TILE);
+    };
+    // Ends phase 2t+1: every copy but this wave's latest batch is complete.
+    auto phase_end_publish = [&] __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmem_n<2 * CPW>();
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    f32x16 sc[2];
+    bf16x8 pb[2][2];
+    // Products of step t: S(t) = K(t) Q^T when PK & 1, P V of tile t-1 when
+    // PK & 2.  PK = 3: P V products on even slots, score products on odd
+    // ones, LDS operands read L slots ahead; PK = 7: both, one after the
+    // other (fewer registers, for the few masked steps).
+    auto products = [&](int t, auto pk_tag) __attribute__((always_inline)) {
+      constexpr int PK = decltype(pk_tag)::value;
+      const char* kb = kbuf + (t & 3) * TILE;
+      const char* vb = vbuf + ((t + 3) & 3) * TILE;
+      if constexpr (PK == 3) {
+        constexpr int NPV = 4 * DT, NM = 2 * NPV;
         static_assert(2 * KS == NPV, "as many S products as P V products");
-        const uint32_t vbase = lds_addr(vprev), kbase = lds_addr(knext);
-        constexpr int L = 3;
+        const uint32_t vbase = lds_addr(vb), kbase = lds_addr(kb);
+        constexpr int L = 4;
         s16x4 rv[NPV][2];
         bf16x8 rk[NPV];
-        auto issue = [&](auto I) {
+        auto issue = [&](auto I) __attribute__((always_inline)) {
           constexpr int i = decltype(I)::value;
           if constexpr ((i & 1) == 0) {
-            constexpr int pidx = i >> 1, g = pidx / DT, t = pidx % DT;
+            constexpr int pidx = i >> 1, g = pidx / DT, tt = pidx % DT;
             constexpr uint32_t rowoff = (uint32_t)(16 * g * RB);
-            rv[pidx][0] = lds_tr16_issue<rowoff>(vbase + (vl ^ (64 * t)));
-            rv[pidx][1] = lds_tr16_issue<rowoff + 8 * RB>(vbase + (vl ^ (64 * t + 32)));
+            rv[pidx][0] = lds_tr16_issue<rowoff>(vbase + (vl ^ (64 * tt)));
+            rv[pidx][1] = lds_tr16_issue<rowoff + 8 * RB>(vbase + (vl ^ (64 * tt + 32)));
           } else {
             constexpr int q = i >> 1, ks = q >> 1, j = q & 1;
             rk[q] = lds_b128_issue<(uint32_t)(32 * j * RB)>(kbase + (kl ^ (ks << 5)));
           }
         };
         static_for<0, L>([&](auto I) { issue(I); });
-        float ls[2] = {0.f, 0.f};
-        float pv[32];
-        const float nm = -m_ref;
         static_for<0, NM>([&](auto I) {
           constexpr int i = decltype(I)::value;
           if constexpr (i + L < NM) issue(std::integral_constant<int, i + L>{});
@@ -403,51 +430,74 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
           }();
           lds_wait<after>();
           if constexpr ((i & 1) == 0) {
-            constexpr int pidx = i >> 1, g = pidx / DT, t = pidx % DT;
-            oacc[t] = mfma32x32x16(tr_pair_take(rv[pidx]), pin[g >> 1][g & 1], oacc[t]);
+            constexpr int pidx = i >> 1, g = pidx / DT, tt = pidx % DT;
+            oacc[tt] = mfma32x32x16(tr_pair_take(rv[pidx]), pb[g >> 1][g & 1], oacc[tt]);
           } else {
             constexpr int q = i >> 1, ks = q >> 1, j = q & 1;
             lds_ready(rk[q]);
-            sn[j] = mfma32x32x16(rk[q], qf[ks], ks == 0 ? (f32x16){} : sn[j]);
+            sc[j] = mfma32x32x16(rk[q], qf[ks], ks == 0 ? (f32x16){} : sc[j]);
           }
-          static_for<0, EPS>([&](auto E) {
-            constexpr int e = EPS * i + decltype(E)::value;
-            const float x = fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], c, nm));
-            pv[e] = x;
-            ls[e & 1] += x;
-          });
-          if constexpr (((i + 1) * EPS) % 8 == 0) {
-            constexpr int e0 = (i + 1) * EPS - 8, j = e0 >> 4, u = (e0 & 15) >> 3;
-            pout[j][u] = pack_bf16x8(pv[e0], pv[e0 + 1], pv[e0 + 2], pv[e0 + 3],
-                                     pv[e0 + 4], pv[e0 + 5], pv[e0 + 6], pv[e0 + 7]);
-            asm volatile("" : "+v"(pout[j][u]));   // keep the packing in this slot
-          }
-          __builtin_amdgcn_sched_barrier(0);
         });
-        float lsum = ls[0] + ls[1];
-        if (__any(!(lsum <= kSumLimit))) {
-          move_reference(sc);
-          lsum = exp_tile(std::false_type{}, sc, pout);
-        }
-        l_part += lsum;
       } else {
-        if (do_pv) pv_tile(vprev, pin, std::integral_constant<uint32_t, 0>{});
-        if (do_s) scores(knext, sn);
-        if (do_sm) {
-          if (masked) softmax_tile(std::true_type{}, sc, k0, pout);
-          else softmax_tile(std::false_type{}, sc, k0, pout);
-        }
+        if constexpr ((PK & 2) != 0) pv_tile(vb, pb, std::integral_constant<uint32_t, 0>{});
+        if constexpr ((PK & 1) != 0) scores(kb, sc);
+        static_assert(PK < 4 || PK == 7, "product kind");
       }
     };
-    f32x16 sa[2], sb[2];
-    bf16x8 pa[2][2], pb2[2][2];
-    scores(kbuf, sa);
-    int kt = 0;
-    for (; kt + 1 <= nkt; kt += 2) {
-      step(kt, sa, sb, pa, pb2);
-      step(kt + 1, sb, sa, pb2, pa);
+    // Softmax of tile t: SK = 0 none, 1 every key visible, 2 masked.
+    auto softmax = [&](int t, auto sk_tag) __attribute__((always_inline)) {
+      constexpr int SK = decltype(sk_tag)::value;
+      if constexpr (SK == 1) softmax_tile(std::false_type{}, sc, t * kBc, pb);
+      if constexpr (SK == 2) softmax_tile(std::true_type{}, sc, t * kBc, pb);
+    };
+    // One step: the products of step t, then the softmax of tile t, each
+    // ending with its phase barrier.
+    auto step = [&](int t, auto pk_tag, auto sk_tag) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(1);
+      products(t, pk_tag);
+      __builtin_amdgcn_s_setprio(0);
+      if (half == 0) phase_end();
+      else phase_end_publish();
+      softmax(t, sk_tag);
+      copies(t + half);
+      if (half == 0) phase_end_publish();
+      else phase_end();
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    using P7 = std::integral_constant<int, 7>;
+    // Leading tiles every key of which this wave's rows see.
+    const int nfree = __builtin_amdgcn_readfirstlane(
+        CAUSAL ? min((qw0 + qoff + 1) / kBc, Nk / kBc) : Nk / kBc);
+    stage_rows(Kg, 0, kbuf);
+    wait_vmem();
+    __syncthreads();
+    stage_or_skip(Kg, 1, kbuf + TILE);
+    stage_or_skip(Vg, 0, vbuf);
+    // Half B starts one phase late (phase 0 idle); the sections below keep
+    // one path per loop body.
+    if (half == 1) {
+      copies(0);
+      phase_end();
     }
-    if (kt <= nkt) step(kt, sa, sb, pa, pb2);
+    if (nfree > 0) step(0, P1{}, P1{});
+    else step(0, P1{}, P2{});
+    int t = 1;
+    for (; t < nfree; ++t) step(t, P3{}, P1{});
+    for (; t <= nlast; ++t) step(t, P7{}, P2{});
+    // t = nlast + 1: P V of this wave's last tile; later steps only copy
+    // and keep the barrier count.
+    if (t < nkt) {
+      step(t, P2{}, P0{});
+      for (++t; t < nkt; ++t) step(t, P0{}, P0{});
+      products(nkt, P0{});
+    } else {
+      products(nkt, P2{});
+    }
+    if (half == 0) phase_end();
+    wait_vmem();              // no copy may land after the workgroup ends
   } else {
     // Double-buffered K and V of the same tile: step t copies tile t+1 while
     // it computes scores, softmax and P V of tile t.
@@ -456,7 +506,7 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
     // Step kt; `cur_tag` is the buffer holding tile kt (kt & 1), a
     // compile-time constant in the two-step loops so that the buffer's LDS
     // offset is an immediate of every fragment read.
-    auto step = [&](int kt, auto mask_tag, auto cur_tag) {
+    auto step = [&](int kt, auto mask_tag, auto cur_tag) __attribute__((always_inline)) {
       constexpr bool CT = !std::is_same_v<decltype(cur_tag), int>;
       const int cur = cur_tag;
       wait_vmem();
@@ -523,9 +573,11 @@ __global__ __launch_bounds__(256, fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch(const FwdArgs& args, int BH, hipStream_t stream) {
+hipError_t launch(FwdArgs args, int BH, hipStream_t stream) {
+  constexpr int W = fwd_wg_waves<D, CAUSAL>();
+  args.nqt = (args.N + 32 * W - 1) / (32 * W);
   const int grid = args.nqt * BH;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(256), 0, stream, args);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(64 * W), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -543,7 +595,6 @@ hipError_t launch_fwd_cross_bf16(const void* q, const void* k, const void* v, vo
   a.N = s.N;
   a.Nk = Nk;
   a.qoff = s.causal ? Nk - s.N : 0;
-  a.nqt = (s.N + kBr - 1) / kBr;
   a.BH = s.B * s.H;
   a.c = s.scale * kLog2e;
   const int BH = s.B * s.H;
