@@ -72,6 +72,19 @@ def kernel_traffic(name):
     return float(m.group(1)) if cur == h.group(1) else None
 
 
+def warm_up(fn, torch, min_seconds=0.2):
+    """Untimed launches for at least `min_seconds` of wall time: after an idle
+    gap (the CPU baseline, tensor set-up) the shader clock needs load to come
+    back up, and a fixed count of short launches does not give it enough."""
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= min_seconds:
+            return
+
+
 def time_forward_only(fa, torch, B, N, H, d, scale, qk_mult, seed, iters, causal=True):
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
@@ -80,10 +93,7 @@ def time_forward_only(fa, torch, B, N, H, d, scale, qk_mult, seed, iters, causal
     v = torch.randn((B, N, H, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    # as many untimed launches as timed ones: after the idle gap before this
-    # case the clock needs a few milliseconds of load to come back up
-    for _ in range(iters):
-        fa.fa_forward(q, k, v, o, lse, scale, causal)
+    warm_up(lambda: fa.fa_forward(q, k, v, o, lse, scale, causal), torch)
     st = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
     ev[0].record(st)
@@ -114,8 +124,7 @@ def time_decode(fa, torch, B, Nq, Nk, H, d, seed, iters):
     ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, Nq, Nk, d, splits) // 4, dtype=torch.float32,
                      device="cuda")
     scale = d ** -0.5
-    for _ in range(iters):
-        fa.fa_decode(q, k, v, o, lse, ws, scale, True, splits)
+    warm_up(lambda: fa.fa_decode(q, k, v, o, lse, ws, scale, True, splits), torch)
     st = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
     ev[0].record(st)
