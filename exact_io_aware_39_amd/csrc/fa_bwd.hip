@@ -199,6 +199,9 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
 
   uint32_t voff[CPW];
   stage_offsets<D, CPW>(voff, wave, lane, rs);
+  // Wave-uniform (scalar) copy of the wave index for LDS destinations, which
+  // must be uniform.
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
   // Copies of query tile s (rows past N and statistics past N read as zero).
   auto stage = [&](int s, char* slot) {
     const int qi0 = qstart + s * kBq;
@@ -207,12 +210,12 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.dout + base + (int64_t)qi0 * rs, (uint32_t)(rows * rs * 2));
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
-      buffer_to_lds16(rq, voff[i], slot + (wave + 4 * i) * 1024);
-      buffer_to_lds16(rg, voff[i], slot + TILE + (wave + 4 * i) * 1024);
+      buffer_to_lds16(rq, voff[i], slot + (wu + 4 * i) * 1024);
+      buffer_to_lds16(rg, voff[i], slot + TILE + (wu + 4 * i) * 1024);
     }
-    if (wave == 0)
+    if (wu == 0)
       buffer_to_lds4(make_rsrc(nlstat + qi0, (uint32_t)(rows * 4)), lane * 4, slot + 2 * TILE);
-    else if (wave == 1)
+    else if (wu == 1)
       buffer_to_lds4(make_rsrc(dstat + qi0, (uint32_t)(rows * 4)), lane * 4, slot + 2 * TILE + 256);
   };
 
@@ -346,11 +349,12 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 
   uint32_t voff[CPW];
   stage_offsets<D, CPW>(voff, wave, lane, rs);
+  const int wu = __builtin_amdgcn_readfirstlane(wave);   // uniform, for LDS destinations
   auto stage_rows = [&](const __bf16* src, int t, char* dst) {
     const int rows = min(N - t * kBk, kBk);
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src + base + (int64_t)t * kBk * rs, (uint32_t)(rows * rs * 2));
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, voff[i], dst + (wave + 4 * i) * 1024);
+    for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, voff[i], dst + (wu + 4 * i) * 1024);
   };
   auto kslot = [&](int t) { return kbuf + (t % NS) * TILE; };
   auto vslot = [&](int t) { return vbuf + (t % NS) * TILE; };
