@@ -36,7 +36,9 @@ Readings taken where the pages are silent or garbled:
   * A row whose keys are all masked has no softmax; it is defined as O = 0 and
     LSE = -inf (this cannot happen for square causal attention).
   * Decode: the nq query rows are the last nq positions of a sequence of nk
-    keys, so under the causal mask row i sees keys 0 .. nk - nq + i.  The pages
+    keys, so under the causal mask row i sees keys 0 .. nk - nq + i.  The
+    backward of such rows (backward_cross) is the same chain rule over that
+    masked score matrix.  The pages
     give no more detail of FlashDecoding than its name; the reading taken is
     the plainest one that the online softmax supports: the keys are split into
     chunks, each chunk gives a normalised partial output and its LSE, and the
@@ -48,7 +50,7 @@ import numpy as np
 
 __all__ = [
     "scores", "softmax_rows", "forward", "forward_rows", "backward",
-    "forward_bnhd", "backward_bnhd", "decode", "merge_partials",
+    "forward_bnhd", "backward_bnhd", "decode", "merge_partials", "backward_cross",
 ]
 
 
@@ -127,13 +129,14 @@ def merge_partials(o_parts, lse_parts):
     return np.where(empty[:, None], 0.0, o), lse
 
 
-def backward(q, k, v, do, scale, causal):
+def backward(q, k, v, do, scale, causal, rows=None):
     """One head: (dQ, dK, dV) of the loss sum(O * dO), by the chain rule.
 
-    Also returns D_i = sum_j P_ij dP_ij, which equals rowsum(dO * O).
+    rows: absolute query index of each q row, as in :func:`scores` (default
+    0..nq-1).  Also returns D_i = sum_j P_ij dP_ij, which equals rowsum(dO * O).
     """
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
-    p, _, _, _ = softmax_rows(scores(q, k, scale, causal))
+    p, _, _, _ = softmax_rows(scores(q, k, scale, causal, rows=rows))
     dv = p.T @ do
     dp = do @ v.T
     dvec = (p * dp).sum(axis=1)
@@ -141,6 +144,13 @@ def backward(q, k, v, do, scale, causal):
     dq = float(scale) * (ds @ k)
     dk = float(scale) * (ds.T @ q)
     return dq, dk, dv, dvec
+
+
+def backward_cross(q, k, v, do, scale, causal):
+    """Backward of :func:`decode` (nq query rows against len(k) keys, the rows
+    being the last nq positions of the sequence): (dQ, dK, dV, D)."""
+    nq, nk = np.shape(q)[0], np.shape(k)[0]
+    return backward(q, k, v, do, scale, causal, rows=np.arange(nk - nq, nk))
 
 
 # ----------------------------------------------------------------- [B, N, H, d] helpers

@@ -18,6 +18,9 @@ invariant, a library routine or a numerical derivative.  Sources:
     satisfy sum_j dK_j = 0, sum_j dV_j = sum_i dO_i and D = rowsum(dO * O).
   * The worked rescale example of the page "Flash Attention 到底做了什么？"
     (guanweilu.cn) has the closed form l = e^-5 (1 + e^-10 + e^-20) + 1.
+  * The backward of rows that are the last positions of a sequence agrees with
+    central finite differences of sum(decode(q, k, v) * dO), and with the
+    square backward of the whole sequence whose other rows have dO = 0.
 """
 from __future__ import annotations
 
@@ -234,8 +237,47 @@ def pin_merge(ora):
     _close(lse_m, [0.3 + math.log(2.0)], 1e-15, "equal-weight merge LSE")
 
 
+def pin_backward_cross(ora):
+    """Gradients of the last nq rows of a sequence of nk keys."""
+    rng = _rng(23)
+    nk, nq, d, scale, h = 9, 4, 5, 0.7, 1e-6
+    for causal in (True, False):
+        q, do = rng.standard_normal((nq, d)), rng.standard_normal((nq, d))
+        k, v = rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+        dq, dk, dv, dvec = ora.backward_cross(q, k, v, do, scale, causal)
+
+        def loss(qq, kk, vv):
+            o, _ = ora.decode(qq, kk, vv, scale, causal)
+            return float((o * do).sum())
+
+        for name, x, g in (("dQ", q, dq), ("dK", k, dk), ("dV", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                a_p = {"q": q, "k": k, "v": v}
+                a_m = dict(a_p)
+                a_p[name[1].lower()], a_m[name[1].lower()] = xp, xm
+                num[idx] = (loss(a_p["q"], a_p["k"], a_p["v"]) - loss(a_m["q"], a_m["k"], a_m["v"])) / (2 * h)
+            tol = 1e-6 * max(1.0, float(np.abs(num).max()))
+            _close(g, num, tol, f"cross {name} vs central differences (causal={causal})")
+        o, _ = ora.decode(q, k, v, scale, causal)
+        _close(dvec, (do * o).sum(axis=1), 1e-12, "cross D = rowsum(dO * O)")
+    # The square backward over the whole sequence with dO = 0 on the first
+    # nk - nq rows: those rows contribute nothing to dK and dV.
+    q_full, k, v = (rng.standard_normal((nk, d)) for _ in range(3))
+    do_full = np.zeros((nk, d))
+    do_full[nk - nq:] = rng.standard_normal((nq, d))
+    dq_f, dk_f, dv_f, _ = ora.backward(q_full, k, v, do_full, scale, True)
+    dq_c, dk_c, dv_c, _ = ora.backward_cross(q_full[nk - nq:], k, v, do_full[nk - nq:], scale, True)
+    _close(dq_c, dq_f[nk - nq:], 1e-13, "cross dQ vs last rows of the square backward")
+    _close(dk_c, dk_f, 1e-13, "cross dK vs square backward")
+    _close(dv_c, dv_f, 1e-13, "cross dV vs square backward")
+
+
 ALL_PINS = [
     pin_zero_query, pin_unit_values, pin_permutation, pin_dominant_logit, pin_causal_rows,
     pin_scipy, pin_finite_differences, pin_backward_invariants, pin_worked_example,
-    pin_decode, pin_merge,
+    pin_decode, pin_merge, pin_backward_cross,
 ]

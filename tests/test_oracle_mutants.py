@@ -48,9 +48,9 @@ def _forward_uses_k(q, k, v, scale, causal):
 
 
 def _backward_variant(kind):
-    def backward(q, k, v, do, scale, causal):
+    def backward(q, k, v, do, scale, causal, rows=None):
         q, k, v, do = (np.asarray(x, float) for x in (q, k, v, do))
-        p, _, _, _ = ora.softmax_rows(ora.scores(q, k, scale, causal))
+        p, _, _, _ = ora.softmax_rows(ora.scores(q, k, scale, causal, rows=rows))
         dv = p.T @ do if kind != "dv_untransposed" else p @ do
         dp = do @ v.T
         dvec = (p * dp).sum(axis=1)
@@ -68,6 +68,10 @@ def _backward_variant(kind):
 
 def _decode_aligned_to_start(q, k, v, scale, causal):
     return ora.forward_rows(q, np.arange(np.shape(q)[0]), k, v, scale, causal)
+
+
+def _backward_cross_aligned_to_start(q, k, v, do, scale, causal):
+    return ora.backward(q, k, v, do, scale, causal)
 
 
 def _merge_unweighted(o_parts, lse_parts):
@@ -98,6 +102,7 @@ MUTANTS = {
     "backward_dk_untransposed": ("backward", _backward_variant("dk_untransposed")),
     "backward_dv_untransposed": ("backward", _backward_variant("dv_untransposed")),
     "decode_aligned_to_start": ("decode", _decode_aligned_to_start),
+    "backward_cross_aligned_to_start": ("backward_cross", _backward_cross_aligned_to_start),
     "merge_unweighted": ("merge_partials", _merge_unweighted),
     "merge_lse_is_max": ("merge_partials", _merge_lse_max),
 }
