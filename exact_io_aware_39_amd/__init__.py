@@ -3,6 +3,7 @@
     o, lse = forward(q, k, v, scale=None, causal=False)
     dq, dk, dv = backward(q, k, v, o, do, lse, scale=None, causal=False)
     o, lse = forward_cross(q, k, v, scale=None, causal=False)      # q: [B, Nq, H, d], k: [B, Nk, H, d]
+    dq, dk, dv = backward_cross(q, k, v, o, do, lse, scale=None, causal=False)
     o, lse = decode(q, k, v, scale=None, causal=False, splits=0)   # q: [B, Nq, H, d], Nq <= 32
 
 Tensors are contiguous [B, N, H, d] bf16 (or fp32) CUDA tensors with d in
@@ -15,8 +16,8 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_dkdv, fa_backward_dq,  # noqa: F401
-                   fa_backward_dqdkdv,
+from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_cross, fa_backward_dkdv,  # noqa: F401
+                   fa_backward_dq, fa_backward_dqdkdv,
                    fa_backward_preprocess, fa_backward_workspace_bytes, fa_decode,
                    fa_decode_splits, fa_decode_workspace_bytes, fa_forward, fa_forward_cross,
                    fa_status_string, load)
@@ -51,6 +52,16 @@ def backward(q, k, v, o, do, lse, scale=None, causal=False, stream=None):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device=q.device)
     fa_backward(q, k, v, o, do, lse, dq, dk, dv, ws, _scale(q, scale), causal, stream)
+    return dq, dk, dv
+
+
+def backward_cross(q, k, v, o, do, lse, scale=None, causal=False, stream=None):
+    """dQ, dK, dV of sum(O * dO) for forward_cross (Nq query rows against Nk
+    keys); allocates the outputs and the workspace."""
+    B, Nq, H, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa_backward_workspace_bytes(B, H, Nq, d) // 4, dtype=torch.float32, device=q.device)
+    fa_backward_cross(q, k, v, o, do, lse, dq, dk, dv, ws, _scale(q, scale), causal, stream)
     return dq, dk, dv
 
 

@@ -53,6 +53,8 @@ def load() -> ctypes.CDLL:
     lib.fa_backward_workspace_bytes.restype = S
     lib.fa_forward_cross.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.fa_forward_cross.restype = I
+    lib.fa_backward_cross.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P]
+    lib.fa_backward_cross.restype = I
     lib.fa_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.fa_decode.restype = I
     lib.fa_decode_splits.argtypes = [I, I, I, I, I]
@@ -194,6 +196,23 @@ def fa_decode(q, k, v, o, lse, workspace, scale: float, causal: bool, splits: in
     _call("fa_decode", load().fa_decode(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), B, H, Nq, Nk, d,
         float(scale), int(bool(causal)), int(splits), _stream(stream)))
+
+
+def fa_backward_cross(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float, causal: bool, stream=None):
+    """fa_backward_cross: q, o, do, dq [B, Nq, H, d] and k, v, dk, dv [B, Nk, H, d] bf16;
+    lse [B, H, Nq] and the workspace fp32."""
+    B, Nq, H, d = _shape(q)
+    Bk, Nk, Hk, dk_ = _shape(k)
+    if (Bk, Hk, dk_) != (B, H, d) or any(tuple(t.shape) != tuple(k.shape) for t in (v, dk, dv)) \
+            or any(tuple(t.shape) != tuple(q.shape) for t in (o, do, dq)):
+        raise ValueError("fa_backward_cross: q/o/do/dq and k/v/dk/dv must share B, H and d")
+    _check((q, k, v, o, do, dq, dk, dv), torch.bfloat16)
+    _check((lse, workspace), torch.float32)
+    if workspace.numel() * 4 < fa_backward_workspace_bytes(B, H, Nq, d):
+        raise ValueError("workspace smaller than fa_backward_workspace_bytes(B, H, Nq, d)")
+    _call("fa_backward_cross", load().fa_backward_cross(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), B, H, Nq, Nk, d, float(scale), int(bool(causal)), _stream(stream)))
 
 
 def fa_forward_cross(q, k, v, o, lse, scale: float, causal: bool, stream=None):

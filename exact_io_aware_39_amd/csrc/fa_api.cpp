@@ -103,6 +103,19 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
                                        static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_backward_cross(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                            const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
+                            int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  fa_status st = check_common(B, H, Nq, d, scale, causal);
+  if (st == FA_OK) st = check_common(B, H, Nk, d, scale, causal);
+  if (st == FA_OK && causal && Nq > Nk) st = FA_ERR_INVALID_ARG;
+  if (st == FA_OK) st = check_tensors({Q, K, V, O, dO, dQ, dK, dV}, {LSE, workspace});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, Nq, d, scale, causal};
+  return to_status(fa::launch_bwd_cross_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, s, Nk,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_backward_preprocess(const void* O, const void* dO, const float* LSE, float* workspace,
                                  int B, int H, int N, int d, void* stream) {
   fa_status st = check_common(B, H, N, d, 1.f, 0);

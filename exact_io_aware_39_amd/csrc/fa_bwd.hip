@@ -50,7 +50,9 @@ struct BwdArgs {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  int H, N, ntiles, BH;
+  int H, N, ntiles, BH;   // N: query rows per head
+  int Nk;             // key rows per head
+  int qoff;           // sequence position of query row 0 (causal: Nk - N)
   int64_t bhn;        // B*H*N
   float c;            // scale * log2(e)
   float scale;
@@ -170,9 +172,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int N = a.N;
+  const int N = a.N, Nk = a.Nk, qoff = a.qoff;
   const int64_t rs = (int64_t)a.H * D;
-  const int64_t base = ((int64_t)b * N * a.H + h) * D;
+  const int64_t base = ((int64_t)b * N * a.H + h) * D;      // Q, dO
+  const int64_t kbase = ((int64_t)b * Nk * a.H + h) * D;    // K, V, dK, dV
   const float* dstat = a.ws + (int64_t)bh * N;
   const float* nlstat = a.ws + a.bhn + (int64_t)bh * N;
 
@@ -183,18 +186,20 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
   // K^T and V^T as B operands: this lane's key, chunk 2 ks + hh.
   bf16x8 kf[KS], vf[KS];
   {
-    const int64_t kr = min(mykey, N - 1);
+    const int64_t kr = min(mykey, Nk - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = *reinterpret_cast<const bf16x8*>(a.k + base + kr * rs + (2 * ks + hh) * 8);
-      vf[ks] = *reinterpret_cast<const bf16x8*>(a.v + base + kr * rs + (2 * ks + hh) * 8);
+      kf[ks] = *reinterpret_cast<const bf16x8*>(a.k + kbase + kr * rs + (2 * ks + hh) * 8);
+      vf[ks] = *reinterpret_cast<const bf16x8*>(a.v + kbase + kr * rs + (2 * ks + hh) * 8);
     }
   }
   f32x16 dk[DT], dv[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) { dk[t] = (f32x16){}; dv[t] = (f32x16){}; }
 
-  const int qstart = CAUSAL ? k0 : 0;
+  // Under the mask query row i (sequence position i + qoff) sees keys up to
+  // i + qoff: the first row that can see key k0 is k0 - qoff.
+  const int qstart = CAUSAL ? max(0, k0 - qoff) : 0;
   const int nsteps = (N - qstart + kBq - 1) / kBq;
 
   uint32_t voff[CPW];
@@ -255,7 +260,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
           float pv = fast_exp2(__builtin_fmaf(sacc[r], c, nl[e]));
           if constexpr (MASK) {
             const int qrow = qi0 + 8 * g4 + 4 * hh + e;
-            const bool hide = qrow >= N || (CAUSAL && mykey > qrow);
+            const bool hide = qrow >= N || (CAUSAL && mykey > qrow + qoff);
             pv = hide ? 0.f : pv;
           }
           p[4 * g + e] = pv;
@@ -274,8 +279,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
   };
   auto update_tile = [&](const char* slot, const f32x16& sacc, const f32x16& pacc, int s) {
     const int qi0 = qstart + s * kBq;
-    if (CAUSAL && qi0 + kBq - 1 < kw0) return;   // every query precedes this wave's keys
-    const bool masked = (qi0 + kBq > N) || (CAUSAL && kw0 + 31 > qi0);
+    if (CAUSAL && qi0 + kBq - 1 + qoff < kw0) return;   // every query precedes this wave's keys
+    const bool masked = (qi0 + kBq > N) || (CAUSAL && kw0 + 31 > qi0 + qoff);
     if (__builtin_expect(masked, 0)) update(std::true_type{}, slot, sacc, pacc, qi0);
     else update(std::false_type{}, slot, sacc, pacc, qi0);
   };
@@ -287,15 +292,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
     __syncthreads();
     if (s + 1 < nsteps) stage(s + 1, smem + ((s + 1) & 1) * SLOT);
     const int qi0 = qstart + s * kBq;
-    if (CAUSAL && qi0 + kBq - 1 < kw0) continue;
+    if (CAUSAL && qi0 + kBq - 1 + qoff < kw0) continue;
     f32x16 sacc, pacc;
     scores(slot, sacc, pacc);
     update_tile(slot, sacc, pacc, s);
   }
 
-  if (mykey < N) {
-    store_row_frags<D>(a.dk + base + (int64_t)mykey * rs, dk, hh, a.scale);
-    store_row_frags<D>(a.dv + base + (int64_t)mykey * rs, dv, hh, 1.f);
+  if (mykey < Nk) {
+    store_row_frags<D>(a.dk + kbase + (int64_t)mykey * rs, dk, hh, a.scale);
+    store_row_frags<D>(a.dv + kbase + (int64_t)mykey * rs, dv, hh, 1.f);
   }
 }
 
@@ -322,9 +327,10 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int N = a.N;
+  const int N = a.N, Nk = a.Nk, qoff = a.qoff;
   const int64_t rs = (int64_t)a.H * D;
-  const int64_t base = ((int64_t)b * N * a.H + h) * D;
+  const int64_t base = ((int64_t)b * N * a.H + h) * D;      // Q, dO, dQ
+  const int64_t kbase = ((int64_t)b * Nk * a.H + h) * D;    // K, V
 
   const int q0 = qtile * kQPerWg;
   const int qw0 = q0 + 32 * wave;
@@ -344,15 +350,15 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 #pragma unroll
   for (int t = 0; t < DT; ++t) dq[t] = (f32x16){};
 
-  const int kend = CAUSAL ? min(N, q0 + kQPerWg) : N;
+  const int kend = CAUSAL ? min(Nk, q0 + qoff + kQPerWg) : Nk;
   const int nkt = (kend + kBk - 1) / kBk;
 
   uint32_t voff[CPW];
   stage_offsets<D, CPW>(voff, wave, lane, rs);
   const int wu = __builtin_amdgcn_readfirstlane(wave);   // uniform, for LDS destinations
   auto stage_rows = [&](const __bf16* src, int t, char* dst) {
-    const int rows = min(N - t * kBk, kBk);
-    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src + base + (int64_t)t * kBk * rs, (uint32_t)(rows * rs * 2));
+    const int rows = min(Nk - t * kBk, kBk);
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src + kbase + (int64_t)t * kBk * rs, (uint32_t)(rows * rs * 2));
 #pragma unroll
     for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, voff[i], dst + (wu + 4 * i) * 1024);
   };
@@ -385,7 +391,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
         float pv = fast_exp2(__builtin_fmaf(sacc[r], c, nl2));
         if constexpr (MASK) {
           const int key = k0 + 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool hide = key >= N || (CAUSAL && key > myq);
+          const bool hide = key >= Nk || (CAUSAL && key > myq + qoff);
           pv = hide ? 0.f : pv;
         }
         ds[e] = pv * pacc[r];
@@ -408,14 +414,14 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
       stage_rows(a.k, t + 1, kbuf + ((t + 1) & 1) * TILE);
       stage_rows(a.v, t + 1, vbuf + ((t + 1) & 1) * TILE);
     }
-    if (CAUSAL && t * kBk > qw0 + 31) continue;
+    if (CAUSAL && t * kBk > qw0 + qoff + 31) continue;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       f32x16 sc, pc;
       scores(kbuf + (t & 1) * TILE, vbuf + (t & 1) * TILE, j, sc, pc);
       const int k0 = t * kBk;
-      if (CAUSAL && k0 + 32 * j > qw0 + 31) break;
-      const bool masked = (k0 + 32 * j + 32 > N) || (CAUSAL && k0 + 32 * j + 31 > qw0);
+      if (CAUSAL && k0 + 32 * j > qw0 + qoff + 31) break;
+      const bool masked = (k0 + 32 * j + 32 > Nk) || (CAUSAL && k0 + 32 * j + 31 > qw0 + qoff);
       if (__builtin_expect(masked, 0)) update(std::true_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
       else update(std::false_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
     }
@@ -518,7 +524,7 @@ hipError_t run_pre(const BwdArgs& a, int B, hipStream_t st) {
 
 template <int D>
 hipError_t run_dkdv(BwdArgs a, int BH, bool causal, hipStream_t st) {
-  a.ntiles = (a.N + kKeysPerWg - 1) / kKeysPerWg;
+  a.ntiles = (a.Nk + kKeysPerWg - 1) / kKeysPerWg;
   const dim3 grid(a.ntiles * BH);
   if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, dim3(256), 0, st, a);
@@ -536,7 +542,8 @@ hipError_t run_dq(BwdArgs a, int BH, bool causal, hipStream_t st) {
 
 template <int D>
 hipError_t run_fused(BwdArgs a, int BH, bool causal, hipStream_t st) {
-  a.ntiles = (a.N + kKeysPerWg - 1) / kKeysPerWg;   // == query tiles (both 128 rows)
+  // Square attention only (N == Nk): key tiles == query tiles, both 128 rows.
+  a.ntiles = (a.N + kKeysPerWg - 1) / kKeysPerWg;
   const dim3 grid(2 * a.ntiles * BH);
   if (causal) hipLaunchKernelGGL((bwd_fused_kernel<D, true>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((bwd_fused_kernel<D, false>), grid, dim3(256), 0, st, a);
@@ -558,6 +565,8 @@ BwdArgs make_args(const void* q, const void* k, const void* v, const void* o, co
   a.dv = static_cast<__bf16*>(dv);
   a.H = s.H;
   a.N = s.N;
+  a.Nk = s.N;
+  a.qoff = 0;
   a.bhn = (int64_t)s.B * s.H * s.N;
   a.BH = s.B * s.H;
   a.c = s.scale * kLog2e;
@@ -597,6 +606,22 @@ hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const
   const int BH = s.B * s.H;
   return s.d == 64 ? run_dq<64>(a, BH, s.causal != 0, stream)
                    : run_dq<128>(a, BH, s.causal != 0, stream);
+}
+
+hipError_t launch_bwd_cross_bf16(const void* q, const void* k, const void* v, const void* o,
+                                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                 float* ws, const AttnShape& s, int Nk, hipStream_t stream) {
+  hipError_t e = launch_bwd_pre_bf16(o, dout, lse, ws, s, stream);
+  if (e != hipSuccess) return e;
+  if (Nk == s.N) return launch_bwd_dqdkdv_bf16(q, k, v, dout, ws, dq, dk, dv, s, stream);
+  BwdArgs a = make_args(q, k, v, nullptr, dout, nullptr, ws, dq, dk, dv, s);
+  a.Nk = Nk;
+  a.qoff = s.causal ? Nk - s.N : 0;
+  const int BH = s.B * s.H;
+  const bool causal = s.causal != 0;
+  e = s.d == 64 ? run_dkdv<64>(a, BH, causal, stream) : run_dkdv<128>(a, BH, causal, stream);
+  if (e != hipSuccess) return e;
+  return s.d == 64 ? run_dq<64>(a, BH, causal, stream) : run_dq<128>(a, BH, causal, stream);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,

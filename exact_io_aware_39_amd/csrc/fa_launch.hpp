@@ -25,6 +25,11 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
                            float* dvec, const AttnShape& s, hipStream_t stream);
+// Backward with N query rows against Nk key rows (causal: query row i is
+// sequence position Nk - N + i); Nk == N is launch_bwd_bf16.
+hipError_t launch_bwd_cross_bf16(const void* q, const void* k, const void* v, const void* o,
+                                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                 float* ws, const AttnShape& s, int Nk, hipStream_t stream);
 hipError_t launch_bwd_pre_bf16(const void* o, const void* dout, const float* lse, float* ws,
                                const AttnShape& s, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout,

@@ -109,6 +109,20 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
                       int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
+ * Backward of fa_forward_cross, bfloat16 tensors: Q, O, dO, dQ are
+ * [B, Nq, H, d], K, V, dK, dV [B, Nk, H, d], LSE [B, H, Nq] (the forward's,
+ * unchanged).  Masking as in fa_forward_cross (causal = 1: query row i is
+ * sequence position Nk - Nq + i; requires Nq <= Nk).  Same chain rule as
+ * fa_backward; `workspace` holds fa_backward_workspace_bytes(B, H, Nq, d)
+ * bytes and on return its first B*H*Nq floats hold -D.  Nq = Nk runs exactly
+ * what fa_backward runs.  Same checks and limits as fa_forward_cross.
+ */
+fa_status fa_backward_cross(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                            const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
+                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                            void* stream);
+
+/*
  * The three passes fa_backward runs, in this order, for callers that schedule
  * them themselves (bf16 tensors, same layouts and checks as fa_backward):
  *   fa_backward_preprocess  fills `workspace` with -D_i (D_i = sum_c dO_ic O_ic)

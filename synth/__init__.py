@@ -122,14 +122,19 @@ def make_inputs(shape, dtype: str, seed: int, with_do: bool = False, qk_mult: fl
     return out
 
 
-def make_decode_inputs(B: int, Nq: int, Nk: int, H: int, d: int, seed: int, qk_mult: float = 1.0) -> dict:
-    """Seeded Q ([B, Nq, H, d]), K and V ([B, Nk, H, d]) bf16 bits, in that draw order."""
+def make_decode_inputs(B: int, Nq: int, Nk: int, H: int, d: int, seed: int, qk_mult: float = 1.0,
+                       with_do: bool = False) -> dict:
+    """Seeded Q ([B, Nq, H, d]), K and V ([B, Nk, H, d]) and, with with_do, dO
+    ([B, Nq, H, d]) as bf16 bits, in that draw order."""
     rng = np.random.default_rng(seed)
-    return {
+    out = {
         "q": draw((B, Nq, H, d), "bf16", rng, qk_mult),
         "k": draw((B, Nk, H, d), "bf16", rng, qk_mult),
         "v": draw((B, Nk, H, d), "bf16", rng),
     }
+    if with_do:
+        out["do"] = draw((B, Nq, H, d), "bf16", rng)
+    return out
 
 
 def workload_inputs(w: Workload) -> dict:

@@ -50,6 +50,8 @@ def lib():
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_forward_cross.argtypes = [vp] * 5 + [i] * 5 + [f, i, vp]
     lib.fa_forward_cross.restype = i
+    lib.fa_backward_cross.argtypes = [vp] * 10 + [i] * 5 + [f, i, vp]
+    lib.fa_backward_cross.restype = i
     lib.fa_decode.argtypes = [vp] * 6 + [i] * 5 + [f, i, i, vp]
     lib.fa_decode.restype = i
     lib.fa_decode_splits.argtypes = [i] * 5
@@ -64,7 +66,8 @@ def test_header_declares_the_expected_entry_points():
         "fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_f32",
         "fa_backward_preprocess", "fa_backward_dqdkdv", "fa_backward_dkdv", "fa_backward_dq",
         "fa_backward_workspace_bytes", "fa_status_string",
-        "fa_decode", "fa_decode_splits", "fa_decode_workspace_bytes", "fa_forward_cross"])
+        "fa_decode", "fa_decode_splits", "fa_decode_workspace_bytes", "fa_forward_cross",
+        "fa_backward_cross"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -175,6 +178,27 @@ def test_forward_cross_rejects_bad_arguments(lib):
         ptrs[i] = None
         assert call(ptrs=tuple(ptrs)) == INVALID
         ptrs[i] = P + (2 if i == 4 else 8)
+        assert call(ptrs=tuple(ptrs)) == INVALID
+
+
+def test_backward_cross_rejects_bad_arguments(lib):
+    def call(B=1, H=2, Nq=100, Nk=300, d=64, scale=0.1, causal=1, ptrs=(P,) * 10):
+        return lib.fa_backward_cross(*ptrs, B, H, Nq, Nk, d, scale, causal, None)
+    assert call(d=96) == UNSUPPORTED
+    assert call(Nq=0) == INVALID
+    assert call(Nk=0) == INVALID
+    assert call(Nq=301, causal=1) == INVALID        # more rows than keys under the mask
+    assert call(Nk=(1 << 20) + 1) == UNSUPPORTED
+    assert call(Nq=(1 << 20) + 1, causal=0) == UNSUPPORTED
+    assert call(scale=float("nan")) == INVALID
+    assert call(scale=-0.5) == UNSUPPORTED
+    assert call(causal=3) == INVALID
+    stats = (5, 9)                                   # LSE and workspace: 4-byte alignment
+    for i in range(10):
+        ptrs = [P] * 10
+        ptrs[i] = None
+        assert call(ptrs=tuple(ptrs)) == INVALID
+        ptrs[i] = P + (2 if i in stats else 8)
         assert call(ptrs=tuple(ptrs)) == INVALID
 
 
