@@ -89,6 +89,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   }
 }
 
+// Integer division rounding toward -inf / +inf (b > 0).
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+__device__ __forceinline__ int ceil_div(int a, int b) { return a >= 0 ? (a + b - 1) / b : -((-a) / b); }
+
 // Lane base for the A operand of a row-major tile read 16 bytes per lane:
 // row l%32 (+ 32 j), logical chunk 2 ks + l/32; address = base ^ (ks << 5).
 template <int D>
@@ -277,26 +281,48 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
       }
     }
   };
-  auto update_tile = [&](const char* slot, const f32x16& sacc, const f32x16& pacc, int s) {
-    const int qi0 = qstart + s * kBq;
-    if (CAUSAL && qi0 + kBq - 1 + qoff < kw0) return;   // every query precedes this wave's keys
-    const bool masked = (qi0 + kBq > N) || (CAUSAL && kw0 + 31 > qi0 + qoff);
-    if (__builtin_expect(masked, 0)) update(std::true_type{}, slot, sacc, pacc, qi0);
-    else update(std::false_type{}, slot, sacc, pacc, qi0);
-  };
-
-  stage(0, smem);
-  for (int s = 0; s < nsteps; ++s) {
+  // One step: publish query tile s, copy tile s+1, then (MODE 1: unmasked,
+  // MODE 2: masked; MODE 0: none of the step's rows sees this wave's keys)
+  // S, dP, P, dS and the dV, dK updates.
+  auto step = [&](int s, auto mode_tag) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_tag)::value;
     char* slot = smem + (s & 1) * SLOT;
     wait_vmem();
     __syncthreads();
     if (s + 1 < nsteps) stage(s + 1, smem + ((s + 1) & 1) * SLOT);
-    const int qi0 = qstart + s * kBq;
-    if (CAUSAL && qi0 + kBq - 1 + qoff < kw0) continue;
-    f32x16 sacc, pacc;
-    scores(slot, sacc, pacc);
-    update_tile(slot, sacc, pacc, s);
+    if constexpr (MODE != 0) {
+      f32x16 sacc, pacc;
+      scores(slot, sacc, pacc);
+      update(std::bool_constant<MODE == 2>{}, slot, sacc, pacc, qstart + s * kBq);
+    }
+  };
+  // The steps run in sections whose loop bodies have one update path (with
+  // the masked and the unmasked update behind a branch inside one loop, the
+  // compiler kept dK and dV in several register sets and copied them every
+  // step):
+  //   [0, s_vis)        no row of the step sees this wave's keys (causal)
+  //   [s_vis, s_unm)    the step straddles the diagonal: masked
+  //   [s_unm, nfull)    every row sees every key of the wave: unmasked
+  //   [.., nsteps)      the step has rows past N: masked
+  const int nfull = (N - qstart) / kBq;
+  int s_vis = 0, s_unm = 0;
+  if constexpr (CAUSAL) {
+    // step s: rows qi0 .. qi0 + kBq - 1 (qi0 = qstart + s kBq) at positions + qoff;
+    // visible when qi0 + kBq - 1 + qoff >= kw0, unmasked when qi0 + qoff >= kw0 + 31.
+    s_vis = min(nsteps, max(0, ceil_div(kw0 - qoff - (kBq - 1) - qstart, kBq)));
+    s_unm = min(nsteps, max(s_vis, ceil_div(kw0 + 31 - qoff - qstart, kBq)));
+    s_vis = __builtin_amdgcn_readfirstlane(s_vis);
+    s_unm = __builtin_amdgcn_readfirstlane(s_unm);
   }
+  using M0 = std::integral_constant<int, 0>;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
+  stage(0, smem);
+  int s = 0;
+  for (; s < s_vis; ++s) step(s, M0{});
+  for (; s < s_unm; ++s) step(s, M2{});
+  for (; s < nfull; ++s) step(s, M1{});
+  for (; s < nsteps; ++s) step(s, M2{});
 
   if (mykey < Nk) {
     store_row_frags<D>(a.dk + kbase + (int64_t)mykey * rs, dk, hh, a.scale);
@@ -404,36 +430,57 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
   };
 
   // Double-buffered K and V of the same tile; step t copies tile t+1 while it
-  // works through the two 32-key units of tile t.
-  stage_rows(a.k, 0, kslot(0));
-  stage_rows(a.v, 0, vslot(0));
-  for (int t = 0; t < nkt; ++t) {
+  // works through the two 32-key units of tile t.  FULL steps are tiles that
+  // every row of this wave sees whole (one unmasked update path); the other
+  // steps (the diagonal, the ragged end, keys past this wave's rows) take the
+  // general path.  Two loops, so that each body has one path (see dkdv_tile).
+  auto step = [&](int t, auto full_tag) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
     if (t + 1 < nkt) {
       stage_rows(a.k, t + 1, kbuf + ((t + 1) & 1) * TILE);
       stage_rows(a.v, t + 1, vbuf + ((t + 1) & 1) * TILE);
     }
-    if (CAUSAL && t * kBk > qw0 + qoff + 31) continue;
+    const int k0 = t * kBk;
+    if constexpr (decltype(full_tag)::value) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      f32x16 sc, pc;
-      scores(kbuf + (t & 1) * TILE, vbuf + (t & 1) * TILE, j, sc, pc);
-      const int k0 = t * kBk;
-      if (CAUSAL && k0 + 32 * j > qw0 + qoff + 31) break;
-      const bool masked = (k0 + 32 * j + 32 > Nk) || (CAUSAL && k0 + 32 * j + 31 > qw0 + qoff);
-      if (__builtin_expect(masked, 0)) update(std::true_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
-      else update(std::false_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
+      for (int j = 0; j < 2; ++j) {
+        f32x16 sc, pc;
+        scores(kbuf + (t & 1) * TILE, vbuf + (t & 1) * TILE, j, sc, pc);
+        update(std::false_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
+      }
+    } else {
+      if (CAUSAL && k0 > qw0 + qoff + 31) return;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f32x16 sc, pc;
+        scores(kbuf + (t & 1) * TILE, vbuf + (t & 1) * TILE, j, sc, pc);
+        if (CAUSAL && k0 + 32 * j > qw0 + qoff + 31) break;
+        const bool masked = (k0 + 32 * j + 32 > Nk) || (CAUSAL && k0 + 32 * j + 31 > qw0 + qoff);
+        if (masked) update(std::true_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
+        else update(std::false_type{}, kbuf + (t & 1) * TILE, j, sc, pc, k0);
+      }
     }
-  }
+  };
+  // Tiles 0 .. t_full - 1 lie whole below Nk and, under the mask, at or below
+  // the position of this wave's first row.
+  int t_full = min(nkt, Nk / kBk);
+  if constexpr (CAUSAL) t_full = min(t_full, max(0, floor_div(qw0 + qoff - (kBk - 1), kBk) + 1));
+  t_full = __builtin_amdgcn_readfirstlane(t_full);
+  stage_rows(a.k, 0, kslot(0));
+  stage_rows(a.v, 0, vslot(0));
+  int t = 0;
+  for (; t < t_full; ++t) step(t, std::true_type{});
+  for (; t < nkt; ++t) step(t, std::false_type{});
 
   if (myq < N) store_row_frags<D>(a.dq + base + (int64_t)myq * rs, dq, hh, a.scale);
 }
 
 // ------------------------------------------------------------------ kernels
 // Waves per SIMD the dK/dV and fused kernels are compiled for (measured on
-// MI355X).  d = 128 causal: 2 (256 registers with a few spilled, 13% faster
-// than 1); d = 128 without mask: 1 (at 2 it spills some 200 registers).
+// MI355X).  d = 128 causal: 2 (256 registers, faster than 1); d = 128 without
+// mask: 1 (the dQ tile needs about 280 registers; at 2 the fused kernel
+// spills some 60).
 template <int D, bool CAUSAL>
 constexpr int bwd_min_waves() {
   return D == 64 ? (CAUSAL ? 3 : 2) : (CAUSAL ? 2 : 1);
