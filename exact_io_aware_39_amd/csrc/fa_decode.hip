@@ -64,7 +64,11 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void decode_split_kernel(De
   static_assert(dec_lds_bytes<D>() >= 2048 + kDecWaves * 32 * D * 4, "merge area");
   __shared__ __attribute__((aligned(1024))) char smem[dec_lds_bytes<D>()];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is made scalar: it picks each wave's K/V blocks and LDS
+  // ring, and a copy's buffer descriptor and LDS destination must be uniform
+  // (with a per-lane index every copy is wrapped in a loop over its values).
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x / a.S, chunk = blockIdx.x - bh * a.S;
   const int b = bh / a.H, h = bh - b * a.H;
