@@ -1,0 +1,137 @@
+"""CPU oracle for the FP8 (e4m3) attention forward.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module; the GPU path never calls it and shares no code
+with it.
+
+Sources (pages, with the part of each page followed):
+  [FAN] page "FlashAttention" (vagrantpi.github.io PKM note), part "效果":
+        the table row of FlashAttention-3 (FP8 goes beyond its bf16 speed-up)
+        and the paragraph under the table (FA3 uses Hopper features, FP8 among
+        them).
+  [XH]  page "知识点13 | FlashAttention深度攻略" (blog.xiaohack.org), part
+        "前沿研究方向": mixed precision with low-precision formats such as FP8.
+  For e4m3 itself the pages give no definition; the format followed is the
+  8-bit floating point E4M3 of the OCP "OFP8" specification: 1 sign bit, 4
+  exponent bits with bias 7, 3 mantissa bits, subnormals when the exponent
+  field is 0, no infinities, the two codes S.1111.111 are NaN, and the largest
+  finite magnitude is 448.
+
+What is computed (the readings taken, since the pages only name FP8):
+  * Q, K and V arrive as e4m3 codes with one fp32 descale factor per tensor
+    (dq, dk, dv): the value of an element is decode(code) * descale.
+  * forward(): the exact attention of those values, in float64:
+        S = scale * dq * dk * Q8 K8^T (causal mask as in the bf16 path),
+        P = softmax(S), O = dv * P V8, LSE = m + ln l.
+    This is the result the method approximates.
+  * forward_quantised_p(): the same, except that the probabilities enter the
+    second product as e4m3 codes, which is what lets both products of the
+    forward run on FP8 matrix units.  The row maximum is taken first, then
+        p_ij = exp(S_ij - m_i)            (float32, as the kernel computes it)
+        Pq_ij = round_e4m3(p_scale * p_ij) (round to nearest, ties to even)
+        O_i = dv * sum_j Pq_ij V8_j / (p_scale * sum_j p_ij)
+    The normaliser uses the unrounded p, so LSE is the same as in forward().
+    p_scale = 2^8 puts p in [0, 1] into [0, 256], inside the normal range of
+    e4m3 (whose largest value is 448) for every p >= 2^-14; the factor cancels
+    in O.  The exponent is formed in float32 from the float64 score rounded to
+    float32, so the rounding decisions are taken in the precision the kernel
+    takes them in.
+  * A single-pass (online softmax) forward rounds each p against the row
+    maximum found so far and rescales the rounded sum later, so it takes the
+    same rounding decisions as forward_quantised_p only for rows whose maximum
+    lies in the first block of keys it visits.  For every row the difference
+    from forward() obeys the bound |round_e4m3(y) - y| <= max(2^-4 y, 2^-10)
+    for 0 <= y <= 448, whatever maximum p was taken against.
+  * round_e4m3 saturates to +-448 (values of p_scale * p never exceed 256).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import scores, softmax_rows
+
+__all__ = ["E4M3_MAX", "decode_e4m3", "round_e4m3", "e4m3_spacing",
+           "forward", "forward_quantised_p"]
+
+E4M3_MAX = 448.0
+_BIAS = 7
+_MANT = 3
+_EMIN = 1 - _BIAS   # exponent of the smallest normal value, 2^-6
+
+
+def decode_e4m3(codes):
+    """Value of each e4m3 code (uint8 array), float64; NaN for S.1111.111."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> _MANT) & 0xF
+    m = c & 0x7
+    normal = np.ldexp(1.0 + m / 8.0, e - _BIAS)
+    sub = np.ldexp(m / 8.0, _EMIN)
+    val = sign * np.where(e == 0, sub, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def e4m3_spacing(x):
+    """Distance between adjacent e4m3 values around |x| (<= 448).
+
+    2^(e - 3) in the binade [2^e, 2^(e+1)) for e >= -6, and 2^-9 below 2^-6.
+    """
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, _EMIN)
+    return np.ldexp(1.0, (e - _MANT).astype(np.int64))
+
+
+def round_e4m3(x):
+    """Nearest e4m3 value (ties to even mantissa), saturating at +-448."""
+    x = np.asarray(x, dtype=np.float64)
+    q = e4m3_spacing(x)
+    # x / q is exact (q a power of two); np.rint rounds half to even, and an
+    # even multiple of the spacing is an even mantissa.  A value that rounds up
+    # to the next power of two lands on that binade's first value.
+    r = np.rint(x / q) * q
+    return np.clip(r, -E4M3_MAX, E4M3_MAX)
+
+
+def _decoded(q8, k8, v8):
+    return decode_e4m3(q8), decode_e4m3(k8), decode_e4m3(v8)
+
+
+def forward(q8, k8, v8, dq, dk, dv, scale, causal):
+    """Exact attention of the dequantised inputs: returns (O, LSE), float64.
+
+    q8: [nq, d] uint8 e4m3 codes; k8, v8: [nk, d]; dq, dk, dv: descales.
+    Rows sit at absolute positions nk - nq .. nk - 1 (nq = nk: square).
+    """
+    q, k, v = _decoded(q8, k8, v8)
+    nq, nk = q.shape[0], k.shape[0]
+    rows = np.arange(nk - nq, nk)
+    s = scores(q * float(dq), k * float(dk), scale, causal, rows=rows)
+    p, _, _, lse = softmax_rows(s)
+    return (p @ v) * float(dv), lse
+
+
+def forward_quantised_p(q8, k8, v8, dq, dk, dv, scale, causal, p_scale=256.0):
+    """Attention with the probabilities rounded to e4m3 before the product with V.
+
+    Returns (O, LSE, aux) where aux holds the float32 exponent arguments
+    x = S - m (natural-log units, [nq, nk]) and the rounded Pq, for the tests'
+    error bounds.  Fully masked rows give O = 0 and LSE = -inf.
+    """
+    q, k, v = _decoded(q8, k8, v8)
+    nq, nk = q.shape[0], k.shape[0]
+    rows = np.arange(nk - nq, nk)
+    s = scores(q * float(dq), k * float(dk), scale, causal, rows=rows)
+    m = np.max(s, axis=1, keepdims=True) if nk else np.full((nq, 1), -np.inf)
+    live = np.isfinite(m[:, 0])
+    s32 = s.astype(np.float32)
+    m32 = np.where(np.isfinite(m), m, 0.0).astype(np.float32)
+    x = (s32 - m32).astype(np.float32)                      # -inf where masked
+    p = np.exp(x).astype(np.float32)                        # float32 decision
+    pq = round_e4m3(np.float64(p_scale) * p.astype(np.float64))
+    l = p.astype(np.float64).sum(axis=1)
+    denom = np.where(live, p_scale * l, 1.0)
+    o = (pq @ v) * float(dv) / denom[:, None]
+    o[~live] = 0.0
+    lse = np.where(live, m[:, 0] + np.log(np.where(live, l, 1.0)), -np.inf)
+    return o, lse, {"x": x, "p": p, "pq": pq, "l": l}

@@ -1,0 +1,86 @@
+"""The FP8 oracle against its pins, and planted mistakes that the pins must catch."""
+import numpy as np
+import pytest
+
+import oracle.fp8 as fp8
+from fp8_pins import FP8_PINS
+
+
+@pytest.mark.parametrize("pin", FP8_PINS, ids=lambda p: p.__name__)
+def test_fp8_oracle_pin(pin):
+    pin(fp8)
+
+
+_orig = {n: getattr(fp8, n) for n in ("decode_e4m3", "round_e4m3", "forward", "forward_quantised_p")}
+
+
+def _decode_bias8(codes):
+    # the e4m3 "fnuz" variant: exponent bias 8, so every value is halved
+    return _orig["decode_e4m3"](codes) / 2.0
+
+
+def _round_toward_zero(x):
+    x = np.asarray(x, dtype=np.float64)
+    q = fp8.e4m3_spacing(x)
+    return np.clip(np.trunc(x / q) * q, -fp8.E4M3_MAX, fp8.E4M3_MAX)
+
+
+def _round_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    q = fp8.e4m3_spacing(x)
+    return np.clip(np.sign(x) * np.floor(np.abs(x) / q + 0.5) * q, -fp8.E4M3_MAX, fp8.E4M3_MAX)
+
+
+def _forward_dv_in_scores(q8, k8, v8, dq, dk, dv, scale, causal):
+    return _orig["forward"](q8, k8, v8, dq * dv, dk, 1.0, scale, causal)
+
+
+def _qp_variant(kind):
+    def forward_quantised_p(q8, k8, v8, dq, dk, dv, scale, causal, p_scale=256.0):
+        o, lse, aux = _orig["forward_quantised_p"](q8, k8, v8, dq, dk, dv, scale, causal, p_scale)
+        v = fp8.decode_e4m3(v8)
+        pq, l = aux["pq"], aux["l"]
+        if kind == "normalise_by_rounded":
+            o = (pq @ v) * dv / pq.sum(axis=1, keepdims=True)
+        elif kind == "no_p_scale":
+            o = (pq @ v) * dv / l[:, None]
+        elif kind == "unrounded":
+            o = (aux["p"].astype(np.float64) @ v) * dv / l[:, None]
+        elif kind == "max_too_low":
+            # p rounded against m - 1 instead of the row maximum m
+            p = np.exp(aux["x"].astype(np.float64) + 1.0)
+            pq = fp8.round_e4m3(p_scale * p)
+            o = (pq @ v) * dv / (p_scale * p.sum(axis=1, keepdims=True))
+        return o, lse, {**aux, "pq": pq}
+    return forward_quantised_p
+
+
+MUTANTS = {
+    "decode_bias_8": ("decode_e4m3", _decode_bias8),
+    "round_toward_zero": ("round_e4m3", _round_toward_zero),
+    "round_ties_away": ("round_e4m3", _round_ties_away),
+    "forward_dv_in_scores": ("forward", _forward_dv_in_scores),
+    "qp_normalised_by_rounded_p": ("forward_quantised_p", _qp_variant("normalise_by_rounded")),
+    "qp_without_p_scale": ("forward_quantised_p", _qp_variant("no_p_scale")),
+    "qp_not_rounded": ("forward_quantised_p", _qp_variant("unrounded")),
+    "qp_wrong_row_maximum": ("forward_quantised_p", _qp_variant("max_too_low")),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_fp8_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(fp8, attr, fn)
+    caught = []
+    for pin in FP8_PINS:
+        try:
+            pin(fp8)
+        except Exception as e:  # a failed check or an error both expose the mistake
+            caught.append(f"{pin.__name__}: {e}")
+    assert caught, f"no pin caught the planted mistake {name}"
+
+
+def test_fp8_unmutated_template_passes(monkeypatch):
+    monkeypatch.setattr(fp8, "forward_quantised_p", _qp_variant("none"))
+    for pin in FP8_PINS:
+        pin(fp8)
