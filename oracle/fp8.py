@@ -36,12 +36,15 @@ What is computed (the readings taken, since the pages only name FP8):
     in O.  The exponent is formed in float32 from the float64 score rounded to
     float32, so the rounding decisions are taken in the precision the kernel
     takes them in.
-  * A single-pass (online softmax) forward rounds each p against the row
-    maximum found so far and rescales the rounded sum later, so it takes the
-    same rounding decisions as forward_quantised_p only for rows whose maximum
-    lies in the first block of keys it visits.  For every row the difference
-    from forward() obeys the bound |round_e4m3(y) - y| <= max(2^-4 y, 2^-10)
-    for 0 <= y <= 448, whatever maximum p was taken against.
+  * forward_quantised_p_online(): the same rounding, taken the way the
+    online softmax of [FAN] "三招" item 2 meets the keys: block by block
+    (blocks of `block` keys, in order, as the B_c-key blocks of [XH] section
+    3), each p rounded against the row maximum m_b found so far, the running
+    sum and the rounded product rescaled by exp(m_old - m_new) when the
+    maximum grows.  It equals forward_quantised_p when every row's maximum
+    lies in its first block.  For every row the difference from forward()
+    obeys |round_e4m3(y) - y| <= max(2^-4 y, 2^-10) for 0 <= y <= 448,
+    whatever maximum p was taken against.
   * round_e4m3 saturates to +-448 (values of p_scale * p never exceed 256).
 """
 from __future__ import annotations
@@ -51,7 +54,7 @@ import numpy as np
 from .attention import scores, softmax_rows
 
 __all__ = ["E4M3_MAX", "decode_e4m3", "round_e4m3", "e4m3_spacing",
-           "forward", "forward_quantised_p"]
+           "forward", "forward_quantised_p", "forward_quantised_p_online"]
 
 E4M3_MAX = 448.0
 _BIAS = 7
@@ -135,3 +138,46 @@ def forward_quantised_p(q8, k8, v8, dq, dk, dv, scale, causal, p_scale=256.0):
     o[~live] = 0.0
     lse = np.where(live, m[:, 0] + np.log(np.where(live, l, 1.0)), -np.inf)
     return o, lse, {"x": x, "p": p, "pq": pq, "l": l}
+
+
+def forward_quantised_p_online(q8, k8, v8, dq, dk, dv, scale, causal, block=64, p_scale=256.0):
+    """forward_quantised_p with p rounded against the running maximum of the
+    online softmax over blocks of `block` keys (see the module notes).
+
+    Returns (O, LSE, aux); aux["x"] holds, per (row, key), the float32
+    exponent argument S - m_b the key's p was formed from (-inf where masked),
+    aux["p"] that p, aux["pq"] its rounded 2^8 p (before any rescale) and
+    aux["l"] the final running sum of p (relative to the final maximum).
+    """
+    q, k, v = _decoded(q8, k8, v8)
+    nq, nk = q.shape[0], k.shape[0]
+    rows = np.arange(nk - nq, nk)
+    s = scores(q * float(dq), k * float(dk), scale, causal, rows=rows)
+    s32 = s.astype(np.float32)
+    m = np.full(nq, -np.inf)              # running maximum (float64 of float32 scores)
+    l = np.zeros(nq)
+    acc = np.zeros((nq, v.shape[1]))
+    xs = np.full((nq, nk), -np.inf, dtype=np.float32)
+    ps = np.zeros((nq, nk), dtype=np.float32)
+    pqs = np.zeros((nq, nk))
+    for j0 in range(0, nk, block):
+        sb = s32[:, j0:j0 + block]
+        m_new = np.maximum(m, sb.max(axis=1).astype(np.float64)) if sb.shape[1] else m
+        grow = np.isfinite(m_new)
+        alpha = np.where(grow & np.isfinite(m), np.exp(np.where(grow, m - m_new, 0.0)), 0.0)
+        acc *= alpha[:, None]
+        l *= alpha
+        m = m_new
+        m32 = np.where(grow, m, 0.0).astype(np.float32)[:, None]
+        x = (sb - m32).astype(np.float32)
+        p = np.exp(x).astype(np.float32)
+        pq = round_e4m3(np.float64(p_scale) * p.astype(np.float64))
+        acc += pq @ v[j0:j0 + block]
+        l += p.astype(np.float64).sum(axis=1)
+        xs[:, j0:j0 + block], ps[:, j0:j0 + block], pqs[:, j0:j0 + block] = x, p, pq
+    live = np.isfinite(m)
+    denom = np.where(live, p_scale * l, 1.0)
+    o = acc * float(dv) / denom[:, None]
+    o[~live] = 0.0
+    lse = np.where(live, m + np.log(np.where(live, l, 1.0)), -np.inf)
+    return o, lse, {"x": xs, "p": ps, "pq": pqs, "l": l}

@@ -19,7 +19,14 @@ bound that follows from the format:
   * A two-key example with scores (2c, c), c = -ln 0.3, so p = (1, 0.3):
     2^8 * 0.3 = 76.8 rounds to 80, O = dv (256 v0 + 80 v1) / (256 * 1.3) and
     LSE = 2c + ln 1.3.
-  * On random inputs the rounded-P result lies within the bound
+  * The online variant equals the final-maximum one when one block holds all
+    keys, and on rows whose maximum lies in the first block.
+  * A three-key online example, blocks of two: scores (0, -c, c), c = -ln 0.3.
+    Block one rounds 2^8 (1, 0.3) to (256, 80) against the maximum 0; block
+    two raises the maximum to c and rescales by e^-c = 0.3, so
+    O = dv (0.3 (256 v_a + 80 v_b) + 256 v_c) / (256 (0.3 (1 + 0.3) + 1)),
+    where rounding against the final maximum would give (80, 24, 256).
+  * On random inputs the rounded-P results (both variants) lie within the bound
     dv sum_j max(2^-4 y_ij, 2^-10) |V_j| / (256 l_i), y = 256 p, of the exact
     one, and the bound is not met trivially (the two differ).
 """
@@ -155,6 +162,7 @@ def pin_rounding_bound(fp8):
     for causal in (False, True):
         o, lse = fp8.forward(q8, k8, v8, 1.1, 0.9, 0.7, d ** -0.5, causal)
         o_q, lse_q, _ = fp8.forward_quantised_p(q8, k8, v8, 1.1, 0.9, 0.7, d ** -0.5, causal)
+        o_o, lse_o, _ = fp8.forward_quantised_p_online(q8, k8, v8, 1.1, 0.9, 0.7, d ** -0.5, causal, block=8)
         q = fp8.decode_e4m3(q8) * 1.1
         k = fp8.decode_e4m3(k8) * 0.9
         s = d ** -0.5 * q @ k.T
@@ -162,13 +170,52 @@ def pin_rounding_bound(fp8):
             s = np.where(np.arange(nk)[None, :] > np.arange(nq)[:, None], -np.inf, s)
         p = np.exp(s - s.max(axis=1, keepdims=True))
         bound = _bound(fp8, p, v8, 0.7) + 1e-6
-        diff = np.abs(o_q - o)
-        assert (diff <= bound).all(), f"rounded-P result outside the rounding bound (causal={causal})"
-        assert diff.max() > 1e-4, "rounding P to e4m3 changed nothing"
-        _close(lse_q, lse, 1e-5, f"LSE does not depend on the rounding (causal={causal})")
+        for name, oo, ll in (("final maximum", o_q, lse_q), ("online", o_o, lse_o)):
+            diff = np.abs(oo - o)
+            assert (diff <= bound).all(), f"{name}: rounded-P result outside the rounding bound (causal={causal})"
+            assert diff.max() > 1e-4, f"{name}: rounding P to e4m3 changed nothing"
+            _close(ll, lse, 1e-5, f"{name}: LSE does not depend on the rounding (causal={causal})")
+
+
+def pin_online_matches_final_max(fp8):
+    rng = np.random.default_rng(8)
+    nq = nk = 40
+    d = 16
+    q8, k8, v8 = (_codes(rng.standard_normal((n, d))) for n in (nq, nk, nk))
+    for causal in (False, True):
+        ref = fp8.forward_quantised_p(q8, k8, v8, 1.0, 1.0, 0.5, d ** -0.5, causal)
+        got = fp8.forward_quantised_p_online(q8, k8, v8, 1.0, 1.0, 0.5, d ** -0.5, causal, block=64)
+        _close(got[0], ref[0], 1e-12, f"online, one block: O (causal={causal})")
+        _close(got[1], ref[1], 1e-12, f"online, one block: LSE (causal={causal})")
+    # a sink key 0 holds every row's maximum: blocks of 8 round as the final maximum does
+    k = rng.standard_normal((nk, d)); k[:, 0] = 0.0; k[0, 0] = 12.0
+    q = rng.standard_normal((nq, d)); q[:, 0] = 4.0
+    q8, k8 = _codes(q), _codes(k)
+    ref = fp8.forward_quantised_p(q8, k8, v8, 1.0, 1.0, 0.5, d ** -0.5, True)
+    got = fp8.forward_quantised_p_online(q8, k8, v8, 1.0, 1.0, 0.5, d ** -0.5, True, block=8)
+    _close(got[0], ref[0], 1e-12, "online, maximum in the first block: O")
+
+
+def pin_online_worked_three_keys(fp8):
+    d = 8
+    c = -math.log(0.3)
+    q = np.zeros((1, d)); q[0, 0] = 1.0
+    k = np.zeros((3, d)); k[1, 0] = -1.0; k[2, 0] = 1.0
+    v = np.zeros((3, d)); v[0, :] = 1.0; v[1, :] = -2.0; v[2, :] = 0.5
+    dv = 0.75
+    o, lse, aux = fp8.forward_quantised_p_online(_codes(q), _codes(k), _codes(v), 1.0, 1.0, dv, c,
+                                                 False, block=2)
+    assert np.array_equal(aux["pq"][0], [256.0, 80.0, 256.0]), f"online Pq = {aux['pq'][0]}"
+    num = 0.3 * (256 * 1.0 + 80 * -2.0) + 256 * 0.5
+    den = 256 * (0.3 * (1 + 0.3) + 1)
+    _close(o, np.full((1, d), dv * num / den), 1e-6, "three-key online example")
+    _close(lse, [c + math.log(0.3 * 1.3 + 1)], 1e-6, "three-key online LSE")
+    _, _, aux_f = fp8.forward_quantised_p(_codes(q), _codes(k), _codes(v), 1.0, 1.0, dv, c, False)
+    assert np.array_equal(aux_f["pq"][0], [80.0, 24.0, 256.0]), f"final-maximum Pq = {aux_f['pq'][0]}"
 
 
 FP8_PINS = [
     pin_decode, pin_round, pin_zero_query, pin_descales, pin_exact_powers_of_two,
-    pin_worked_two_keys, pin_rounding_bound,
+    pin_worked_two_keys, pin_online_matches_final_max, pin_online_worked_three_keys,
+    pin_rounding_bound,
 ]

@@ -11,7 +11,8 @@ def test_fp8_oracle_pin(pin):
     pin(fp8)
 
 
-_orig = {n: getattr(fp8, n) for n in ("decode_e4m3", "round_e4m3", "forward", "forward_quantised_p")}
+_orig = {n: getattr(fp8, n) for n in ("decode_e4m3", "round_e4m3", "forward", "forward_quantised_p",
+                                      "forward_quantised_p_online")}
 
 
 def _decode_bias8(codes):
@@ -55,6 +56,32 @@ def _qp_variant(kind):
     return forward_quantised_p
 
 
+def _online_variant(kind):
+    def forward_quantised_p_online(q8, k8, v8, dq, dk, dv, scale, causal, block=64, p_scale=256.0):
+        if kind == "final_maximum":
+            return _orig["forward_quantised_p"](q8, k8, v8, dq, dk, dv, scale, causal, p_scale)
+        q, k, v = (fp8.decode_e4m3(x) for x in (q8, k8, v8))
+        nq, nk = q.shape[0], k.shape[0]
+        s = fp8.scores(q * dq, k * dk, scale, causal, rows=np.arange(nk - nq, nk)).astype(np.float32)
+        m = np.full(nq, -np.inf); l = np.zeros(nq); acc = np.zeros((nq, v.shape[1]))
+        pqs = np.zeros((nq, nk))
+        for j0 in range(0, nk, block):
+            sb = s[:, j0:j0 + block]
+            m_new = np.maximum(m, sb.max(axis=1))
+            alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
+            if kind != "no_rescale":
+                acc *= alpha[:, None]
+            l *= alpha
+            m = m_new
+            p = np.exp((sb - m[:, None].astype(np.float32)).astype(np.float32))
+            pq = fp8.round_e4m3(p_scale * p.astype(np.float64))
+            acc += pq @ v[j0:j0 + block]
+            l += p.astype(np.float64).sum(axis=1)
+            pqs[:, j0:j0 + block] = pq
+        return acc * dv / (p_scale * l[:, None]), m + np.log(l), {"pq": pqs, "l": l}
+    return forward_quantised_p_online
+
+
 MUTANTS = {
     "decode_bias_8": ("decode_e4m3", _decode_bias8),
     "round_toward_zero": ("round_e4m3", _round_toward_zero),
@@ -64,6 +91,8 @@ MUTANTS = {
     "qp_without_p_scale": ("forward_quantised_p", _qp_variant("no_p_scale")),
     "qp_not_rounded": ("forward_quantised_p", _qp_variant("unrounded")),
     "qp_wrong_row_maximum": ("forward_quantised_p", _qp_variant("max_too_low")),
+    "online_without_rescale": ("forward_quantised_p_online", _online_variant("no_rescale")),
+    "online_rounds_against_final_maximum": ("forward_quantised_p_online", _online_variant("final_maximum")),
 }
 
 
@@ -82,5 +111,11 @@ def test_fp8_mutant_is_caught(name, monkeypatch):
 
 def test_fp8_unmutated_template_passes(monkeypatch):
     monkeypatch.setattr(fp8, "forward_quantised_p", _qp_variant("none"))
+    for pin in FP8_PINS:
+        pin(fp8)
+
+
+def test_fp8_unmutated_online_template_passes(monkeypatch):
+    monkeypatch.setattr(fp8, "forward_quantised_p_online", _online_variant("none"))
     for pin in FP8_PINS:
         pin(fp8)
