@@ -5,6 +5,7 @@
     o, lse = forward_cross(q, k, v, scale=None, causal=False)      # q: [B, Nq, H, d], k: [B, Nk, H, d]
     dq, dk, dv = backward_cross(q, k, v, o, do, lse, scale=None, causal=False)
     o, lse = decode(q, k, v, scale=None, causal=False, splits=0)   # q: [B, Nq, H, d], Nq <= 32
+    o, lse = forward_fp8(q8, k8, v8, descales=(1, 1, 1), scale=None, causal=False)   # e4m3 inputs
 
 Tensors are contiguous [B, N, H, d] bf16 (or fp32) CUDA tensors with d in
 {64, 128}; lse is fp32 [B, H, N].  scale defaults to d**-0.5, as in the PyTorch
@@ -20,7 +21,7 @@ from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_cross, fa_backwar
                    fa_backward_dq, fa_backward_dqdkdv,
                    fa_backward_preprocess, fa_backward_workspace_bytes, fa_decode,
                    fa_decode_splits, fa_decode_workspace_bytes, fa_forward, fa_forward_cross,
-                   fa_status_string, load)
+                   fa_forward_fp8, fa_forward_fp8_workspace_bytes, fa_status_string, load)
 
 
 def _scale(q, scale):
@@ -76,4 +77,18 @@ def decode(q, k, v, scale=None, causal=False, splits=0, stream=None):
     ws = torch.empty(max(1, fa_decode_workspace_bytes(B, H, Nq, Nk, d, splits) // 4),
                      dtype=torch.float32, device=q.device)
     fa_decode(q, k, v, o, lse, ws, _scale(q, scale), causal, splits, stream)
+    return o, lse
+
+
+def forward_fp8(q, k, v, descales=(1.0, 1.0, 1.0), scale=None, causal=False, stream=None):
+    """O (bf16) and LSE of e4m3 inputs (float8_e4m3fn or uint8 codes, [B, N, H, d]);
+    `descales` = (q, k, v) multipliers of the code values.  q may have fewer rows
+    than k and v (causal: the last rows of the sequence).  Allocates the outputs
+    and the V^T workspace."""
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    o = torch.empty((B, Nq, H, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(1, fa_forward_fp8_workspace_bytes(B, H, Nk, d)), dtype=torch.uint8, device=q.device)
+    fa_forward_fp8(q, k, v, *descales, o, lse, ws, _scale(q, scale), causal, stream)
     return o, lse

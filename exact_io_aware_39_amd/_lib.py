@@ -61,6 +61,10 @@ def load() -> ctypes.CDLL:
     lib.fa_decode_splits.restype = I
     lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.fa_decode_workspace_bytes.restype = S
+    lib.fa_forward_fp8.argtypes = [P, P, P, F, F, F, P, P, P, I, I, I, I, I, F, I, P]
+    lib.fa_forward_fp8.restype = I
+    lib.fa_forward_fp8_workspace_bytes.argtypes = [I, I, I, I]
+    lib.fa_forward_fp8_workspace_bytes.restype = S
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -226,3 +230,32 @@ def fa_forward_cross(q, k, v, o, lse, scale: float, causal: bool, stream=None):
     _call("fa_forward_cross", load().fa_forward_cross(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
         int(bool(causal)), _stream(stream)))
+
+
+def fa_forward_fp8_workspace_bytes(B: int, H: int, Nk: int, d: int) -> int:
+    return int(load().fa_forward_fp8_workspace_bytes(B, H, Nk, d))
+
+
+_E4M3_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def fa_forward_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, o, lse, workspace,
+                   scale: float, causal: bool, stream=None):
+    """fa_forward_fp8: q [B, Nq, H, d], k, v [B, Nk, H, d] e4m3 codes (float8_e4m3fn or
+    uint8); o [B, Nq, H, d] bf16; lse [B, H, Nq] fp32; workspace a CUDA byte buffer."""
+    B, Nq, H, d = _shape(q)
+    Bk, Nk, Hk, dk = _shape(k)
+    if (Bk, Hk, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("fa_forward_fp8: q/o and k/v must share B, H and d, k and v the same shape")
+    for t in (q, k, v):
+        if not t.is_cuda or t.dtype not in _E4M3_DTYPES or not t.is_contiguous():
+            raise ValueError(f"fa_forward_fp8: expected contiguous e4m3 CUDA tensors, got {t.dtype} on {t.device}")
+    _check((o,), torch.bfloat16)
+    _check((lse,), torch.float32)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("fa_forward_fp8: workspace must be a contiguous CUDA tensor")
+    if workspace.numel() * workspace.element_size() < fa_forward_fp8_workspace_bytes(B, H, Nk, d):
+        raise ValueError("workspace smaller than fa_forward_fp8_workspace_bytes()")
+    _call("fa_forward_fp8", load().fa_forward_fp8(
+        _ptr(q), _ptr(k), _ptr(v), float(q_descale), float(k_descale), float(v_descale), _ptr(o),
+        _ptr(lse), _ptr(workspace), B, H, Nq, Nk, d, float(scale), int(bool(causal)), _stream(stream)))

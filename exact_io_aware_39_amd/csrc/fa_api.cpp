@@ -83,6 +83,30 @@ fa_status fa_forward_cross(const void* Q, const void* K, const void* V, void* O,
   return to_status(fa::launch_fwd_cross_bf16(Q, K, V, O, LSE, s, Nk, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_forward_fp8(const void* Q, const void* K, const void* V, float q_descale,
+                         float k_descale, float v_descale, void* O, float* LSE, void* workspace,
+                         int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                         void* stream) {
+  fa_status st = check_common(B, H, Nq, d, scale, causal);
+  if (st == FA_OK) st = check_common(B, H, Nk, d, scale, causal);
+  if (st == FA_OK && causal && Nq > Nk) st = FA_ERR_INVALID_ARG;
+  // A non-positive product of descales would turn the -inf of masked scores
+  // into +inf or NaN.
+  for (float x : {q_descale, k_descale, v_descale})
+    if (st == FA_OK && !(std::isfinite(x) && x > 0.f)) st = FA_ERR_INVALID_ARG;
+  if (st == FA_OK && !std::isfinite(scale * q_descale * k_descale)) st = FA_ERR_INVALID_ARG;
+  if (st == FA_OK) st = check_tensors({Q, K, V, O, workspace}, {LSE});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, Nq, d, scale, causal};
+  return to_status(fa::launch_fwd_fp8(Q, K, V, q_descale, k_descale, v_descale, O, LSE, workspace, s,
+                                      Nk, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_forward_fp8_workspace_bytes(int B, int H, int Nk, int d) {
+  if (check_common(B, H, Nk, d, 1.f, 0) != FA_OK) return 0;
+  return fa::fwd_fp8_workspace_bytes(B, H, Nk, d);
+}
+
 fa_status fa_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
                          int B, int H, int N, int d, float scale, int causal, void* stream) {
   fa_status st = check_common(B, H, N, d, scale, causal);

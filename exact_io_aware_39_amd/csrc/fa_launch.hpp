@@ -20,6 +20,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 // i is sequence position Nk - N + i.
 hipError_t launch_fwd_cross_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                  const AttnShape& s, int Nk, hipStream_t stream);
+// FP8 forward (e4m3 Q, K, V with descales); `ws` holds V^T, fwd_fp8_workspace_bytes.
+size_t fwd_fp8_workspace_bytes(int B, int H, int Nk, int d);
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, float dq, float dk, float dv,
+                          void* o, float* lse, void* ws, const AttnShape& s, int Nk, hipStream_t stream);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           const AttnShape& s, hipStream_t stream);
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,

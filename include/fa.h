@@ -88,6 +88,36 @@ fa_status fa_forward_cross(const void* Q, const void* K, const void* V, void* O,
                            void* stream);
 
 /*
+ * Forward on FP8 inputs (page "FlashAttention", part "效果": FlashAttention-3
+ * and its FP8 mode; page "知识点13 | FlashAttention深度攻略", part
+ * "前沿研究方向": mixed precision with FP8).  Q is [B, Nq, H, d], K and V are
+ * [B, Nk, H, d], each element one byte: an OCP E4M3 code (bias 7, largest
+ * magnitude 448, S.1111.111 = NaN, which propagates).  The value of an
+ * element is its code's value times the tensor's descale (q_descale,
+ * k_descale, v_descale: finite and > 0, else FA_ERR_INVALID_ARG).  Writes O
+ * (bf16, [B, Nq, H, d]) and LSE (fp32, [B, H, Nq]) of
+ *   O = softmax(scale * q_descale * k_descale * Q K^T [+ mask]) V * v_descale.
+ * Both products run on FP8 matrix units with fp32 accumulation: the
+ * probabilities enter the second one as E4M3 codes of 2^8 p, p taken against
+ * the exact running row maximum (rounded to nearest, ties to even); the row
+ * sum and LSE use the unrounded p.  The per-element error this adds to O is at
+ * most v_descale * sum_j max(2^-4 2^8 p_ij, 2^-10) |V_j| / (2^8 l_i).
+ * Masking as in fa_forward_cross (causal = 1: query row i is sequence
+ * position Nk - Nq + i; requires Nq <= Nk).  `workspace` is caller-owned
+ * device memory of fa_forward_fp8_workspace_bytes(B, H, Nk, d) bytes (a
+ * transposed copy of V, [B H, d, Nk rounded up to 64], rewritten by every
+ * call).  Pointers: Q, K, V, O, workspace 16-byte aligned, LSE 4-byte.  Same
+ * shape limits as fa_forward_cross.
+ */
+fa_status fa_forward_fp8(const void* Q, const void* K, const void* V, float q_descale,
+                         float k_descale, float v_descale, void* O, float* LSE, void* workspace,
+                         int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                         void* stream);
+
+/* Bytes of workspace fa_forward_fp8 needs: B H d (Nk rounded up to 64) (0 for invalid sizes). */
+size_t fa_forward_fp8_workspace_bytes(int B, int H, int Nk, int d);
+
+/*
  * Forward, float32 tensors: same contract as fa_forward with every tensor
  * float32 (fp32 products and accumulation throughout).
  */

@@ -146,8 +146,10 @@ def forward_quantised_p_online(q8, k8, v8, dq, dk, dv, scale, causal, block=64, 
 
     Returns (O, LSE, aux); aux["x"] holds, per (row, key), the float32
     exponent argument S - m_b the key's p was formed from (-inf where masked),
-    aux["p"] that p, aux["pq"] its rounded 2^8 p (before any rescale) and
-    aux["l"] the final running sum of p (relative to the final maximum).
+    aux["p"] that p, aux["pq"] its rounded 2^8 p (before any rescale),
+    aux["mref"] the maximum m_b it was taken against (-inf before the row's
+    first visible key), aux["m"] the final maximum and aux["l"] the final
+    running sum of p (relative to the final maximum).
     """
     q, k, v = _decoded(q8, k8, v8)
     nq, nk = q.shape[0], k.shape[0]
@@ -160,6 +162,7 @@ def forward_quantised_p_online(q8, k8, v8, dq, dk, dv, scale, causal, block=64, 
     xs = np.full((nq, nk), -np.inf, dtype=np.float32)
     ps = np.zeros((nq, nk), dtype=np.float32)
     pqs = np.zeros((nq, nk))
+    mref = np.full((nq, nk), -np.inf)
     for j0 in range(0, nk, block):
         sb = s32[:, j0:j0 + block]
         m_new = np.maximum(m, sb.max(axis=1).astype(np.float64)) if sb.shape[1] else m
@@ -175,9 +178,10 @@ def forward_quantised_p_online(q8, k8, v8, dq, dk, dv, scale, causal, block=64, 
         acc += pq @ v[j0:j0 + block]
         l += p.astype(np.float64).sum(axis=1)
         xs[:, j0:j0 + block], ps[:, j0:j0 + block], pqs[:, j0:j0 + block] = x, p, pq
+        mref[:, j0:j0 + block] = m[:, None]
     live = np.isfinite(m)
     denom = np.where(live, p_scale * l, 1.0)
     o = acc * float(dv) / denom[:, None]
     o[~live] = 0.0
     lse = np.where(live, m + np.log(np.where(live, l, 1.0)), -np.inf)
-    return o, lse, {"x": xs, "p": ps, "pq": pqs, "l": l}
+    return o, lse, {"x": xs, "p": ps, "pq": pqs, "mref": mref, "m": m, "l": l}

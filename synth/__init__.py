@@ -137,6 +137,50 @@ def make_decode_inputs(B: int, Nq: int, Nk: int, H: int, d: int, seed: int, qk_m
     return out
 
 
+def to_e4m3(x: np.ndarray):
+    """Per-tensor e4m3 quantisation of float32 values: the descale maps max |x|
+    to 448 (the largest e4m3 magnitude), codes are x / descale rounded to
+    nearest even by torch's float8_e4m3fn conversion.  Returns (codes as
+    uint8, descale as a float32 value)."""
+    import torch
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    descale = f32(amax / 448.0) if amax > 0 else 1.0
+    y = torch.from_numpy(np.ascontiguousarray(x / np.float32(descale), dtype=np.float32))
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), descale
+
+
+def make_fp8_inputs(B: int, Nq: int, Nk: int, H: int, d: int, seed: int, sink: float = 0.0,
+                    qk_int: bool = False) -> dict:
+    """Seeded e4m3 Q ([B, Nq, H, d]), K and V ([B, Nk, H, d]) with their descales.
+
+    Q, K, V are drawn as float32 standard normals in that order and quantised
+    per tensor (to_e4m3).  qk_int: Q and K become the integers
+    clip(rint(4 x), -15, 15) with descale 1/4 instead (every such integer is
+    an e4m3 value, and the scores are sums of integer products).  sink > 0
+    adds an attention-sink key: the last feature of every query is 2, that of
+    key 0 is `sink` and that of every other key 0 (before quantisation).
+    Returns {"q", "k", "v": uint8 codes, "descales": (dq, dk, dv)}."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Nq, H, d), dtype=np.float32)
+    k = rng.standard_normal((B, Nk, H, d), dtype=np.float32)
+    v = rng.standard_normal((B, Nk, H, d), dtype=np.float32)
+    if sink > 0:
+        q[..., d - 1] = 2.0
+        k[..., d - 1] = 0.0
+        k[:, 0, :, d - 1] = sink
+    if qk_int:
+        import torch
+
+        def ints(x):
+            t = torch.from_numpy(np.clip(np.rint(4 * x), -15, 15).astype(np.float32))
+            return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        q8, k8, dq, dk = ints(q), ints(k), 0.25, 0.25
+    else:
+        (q8, dq), (k8, dk) = to_e4m3(q), to_e4m3(k)
+    v8, dv = to_e4m3(v)
+    return {"q": q8, "k": k8, "v": v8, "descales": (dq, dk, dv)}
+
+
 def workload_inputs(w: Workload) -> dict:
     return make_inputs(w.shape, w.dtype, w.seed, with_do=w.backward, qk_mult=w.qk_mult)
 

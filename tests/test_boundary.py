@@ -58,6 +58,10 @@ def lib():
     lib.fa_decode_splits.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i] * 6
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_forward_fp8.argtypes = [vp] * 3 + [f] * 3 + [vp] * 3 + [i] * 5 + [f, i, vp]
+    lib.fa_forward_fp8.restype = i
+    lib.fa_forward_fp8_workspace_bytes.argtypes = [i] * 4
+    lib.fa_forward_fp8_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -67,7 +71,7 @@ def test_header_declares_the_expected_entry_points():
         "fa_backward_preprocess", "fa_backward_dqdkdv", "fa_backward_dkdv", "fa_backward_dq",
         "fa_backward_workspace_bytes", "fa_status_string",
         "fa_decode", "fa_decode_splits", "fa_decode_workspace_bytes", "fa_forward_cross",
-        "fa_backward_cross"])
+        "fa_backward_cross", "fa_forward_fp8", "fa_forward_fp8_workspace_bytes"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -179,6 +183,39 @@ def test_forward_cross_rejects_bad_arguments(lib):
         assert call(ptrs=tuple(ptrs)) == INVALID
         ptrs[i] = P + (2 if i == 4 else 8)
         assert call(ptrs=tuple(ptrs)) == INVALID
+
+
+def test_forward_fp8_rejects_bad_arguments(lib):
+    def call(B=1, H=2, Nq=100, Nk=300, d=64, scale=0.1, causal=1, ds=(0.5, 0.5, 0.5), ptrs=(P,) * 6):
+        q, k, v, o, lse, ws = ptrs
+        return lib.fa_forward_fp8(q, k, v, *ds, o, lse, ws, B, H, Nq, Nk, d, scale, causal, None)
+    assert call(d=96) == UNSUPPORTED
+    assert call(Nq=0) == INVALID
+    assert call(Nk=0) == INVALID
+    assert call(Nq=301, causal=1) == INVALID
+    assert call(Nk=(1 << 20) + 1) == UNSUPPORTED
+    assert call(scale=float("inf")) == INVALID
+    assert call(causal=2) == INVALID
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        for j in range(3):
+            ds = [0.5, 0.5, 0.5]
+            ds[j] = bad
+            assert call(ds=tuple(ds)) == INVALID, (j, bad)
+    assert call(scale=3e38, ds=(1e10, 1e10, 1.0)) == INVALID    # scale * dq * dk overflows
+    for j in range(6):
+        ptrs = [P] * 6
+        ptrs[j] = None
+        assert call(ptrs=tuple(ptrs)) == INVALID
+        ptrs[j] = P + (2 if j == 4 else 8)
+        assert call(ptrs=tuple(ptrs)) == INVALID
+
+
+def test_forward_fp8_workspace_bytes(lib):
+    assert lib.fa_forward_fp8_workspace_bytes(4, 16, 4096, 128) == 4 * 16 * 128 * 4096
+    assert lib.fa_forward_fp8_workspace_bytes(1, 2, 65, 64) == 2 * 64 * 128
+    assert lib.fa_forward_fp8_workspace_bytes(1, 1, 1, 64) == 64 * 64
+    assert lib.fa_forward_fp8_workspace_bytes(1, 1, 0, 64) == 0
+    assert lib.fa_forward_fp8_workspace_bytes(1, 1, 64, 96) == 0
 
 
 def test_backward_cross_rejects_bad_arguments(lib):

@@ -1,0 +1,122 @@
+"""GPU parity of fa_forward_fp8 (e4m3 Q, K, V with per-tensor descales).
+
+Each head is compared with the FP8 oracles of oracle/fp8.py under the bounds of
+tests/fp8_bounds.py: every row against the exact attention of the dequantised
+inputs (forward) within the rounding bound, and, for inputs whose Q and K are
+integer-coded (exact scores), every row against the online rounded-P oracle
+(forward_quantised_p_online, 64-key blocks) within the tight bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_39_amd as fa
+import oracle.fp8 as fp8
+import synth
+from fp8_bounds import lse_bound, loose_bound, tight_bound
+from gpu_helpers import require_gpu, say, to64
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, Nq, Nk, H, d, causal, integer-coded Q and K
+    (1, 256, 256, 2, 64, True, True),
+    (2, 333, 333, 2, 128, False, True),
+    (2, 333, 333, 2, 128, False, False),
+    (1, 100, 1000, 2, 128, True, True),      # the last 100 positions of 1000
+    (1, 1000, 1000, 1, 64, True, True),
+    (1, 1000, 1000, 1, 64, True, False),
+    (1, 500, 200, 2, 64, False, True),       # more query rows than keys
+    (1, 64, 64, 1, 128, True, True),         # one tile
+    (1, 1, 4097, 2, 128, True, True),        # one row, ragged key tail
+    (2, 129, 4097, 3, 64, False, True),
+    (1, 700, 1500, 2, 128, False, False),
+    (1, 1, 1, 1, 64, False, True),           # one key
+]
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _check_rows(o, lse, q8, k8, v8, descales, scale, causal, exact, what):
+    """Bounds for one head (o: [nq, d], lse: [nq]); returns the largest
+    error-to-bound ratios (loose, tight) and the number of ambiguous p."""
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), f"{what}: non-finite output"
+    o_ex, lse_ex = fp8.forward(q8, k8, v8, *descales, scale, causal)
+    lb = loose_bound(q8, k8, v8, descales, scale, causal, o_ex, exact)
+    err = np.abs(o - o_ex)
+    assert (err <= lb).all(), (f"{what}: O outside the rounding bound by "
+                               f"{(err - lb).max():.3e} (max err {err.max():.3e})")
+    lerr = np.abs(lse - lse_ex)
+    assert (lerr <= lse_bound(q8, k8, descales, scale, causal, lse_ex, exact)).all(), \
+        f"{what}: LSE err {lerr.max():.3e} above its bound"
+    ratio_tight, namb = 0.0, 0
+    if exact:
+        o_on, _, aux = fp8.forward_quantised_p_online(q8, k8, v8, *descales, scale, causal, block=64)
+        tb, namb = tight_bound(q8, k8, v8, descales, scale, causal, o_on, aux, True)
+        terr = np.abs(o - o_on)
+        assert (terr <= tb).all(), (f"{what}: O differs from the online rounded-P oracle by "
+                                    f"{terr.max():.3e}, {(terr - tb).max():.3e} above the tight bound")
+        ratio_tight = float((terr / tb).max())
+    return float((err / lb).max()), ratio_tight, namb
+
+
+@pytest.mark.parametrize("B,Nq,Nk,H,d,causal,qk_int", CASES)
+def test_forward_fp8_matches_oracles(B, Nq, Nk, H, d, causal, qk_int):
+    require_gpu()
+    say("forward_fp8", B, Nq, Nk, H, d, causal, qk_int)
+    host = synth.make_fp8_inputs(B, Nq, Nk, H, d, seed=3000 + Nq + 7 * Nk + d, qk_int=qk_int)
+    q, k, v = (_dev(host[x]).view(torch.float8_e4m3fn) for x in "qkv")
+    descales = host["descales"]
+    scale = synth.f32(d ** -0.5)
+    o, lse = fa.forward_fp8(q, k, v, descales=descales, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o64, lse64 = to64(o), to64(lse)
+    worst = [0.0, 0.0, 0]
+    for b in range(B):
+        for h in range(H):
+            r = _check_rows(o64[b, :, h], lse64[b, h], host["q"][b, :, h], host["k"][b, :, h],
+                            host["v"][b, :, h], descales, scale, causal, qk_int, f"(b={b}, h={h})")
+            worst = [max(worst[0], r[0]), max(worst[1], r[1]), worst[2] + r[2]]
+    say(f"  error / bound: loose {worst[0]:.3f}, tight {worst[1]:.3f}; ambiguous p {worst[2]}")
+
+
+def test_forward_fp8_full_size_sampled_rows():
+    """[4, 4096, 16, 128] causal (the bf16 forward's workload shape), launched as
+    the benchmark launches it; sampled rows of two heads against the oracles
+    (row i of a causal square problem is the last row of keys 0 .. i)."""
+    require_gpu()
+    B, N, H, d = 4, 4096, 16, 128
+    say("forward_fp8 full size", B, N, H, d)
+    host = synth.make_fp8_inputs(B, N, N, H, d, seed=3, qk_int=True)
+    q, k, v = (_dev(host[x]).view(torch.float8_e4m3fn) for x in "qkv")
+    descales = host["descales"]
+    scale = synth.f32(d ** -0.5)
+    o, lse = fa.forward_fp8(q, k, v, descales=descales, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    o64, lse64 = to64(o), to64(lse)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, N - 1], rng.integers(0, N, 24)]))
+    for (b, h) in [(0, 0), (B - 1, H - 1)]:
+        for i in rows:
+            _check_rows(o64[b, i:i + 1, h], lse64[b, h, i:i + 1], host["q"][b, i:i + 1, h],
+                        host["k"][b, :i + 1, h], host["v"][b, :i + 1, h], descales, scale, True, True,
+                        f"(b={b}, h={h}, row={i})")
+
+
+def test_forward_fp8_exact_tile_representable():
+    """Scores whose probabilities are powers of two (2^8 p exact in e4m3) and
+    V = 1: O = v_descale exactly up to bf16 rounding, whatever the rounding."""
+    require_gpu()
+    B, N, H, d = 1, 200, 1, 64
+    q = np.zeros((B, N, H, d), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((B, N, H, d), np.float32)
+    k[:, :, 0, 0] = -(np.arange(N) % 9)
+    v = np.ones((B, N, H, d), np.float32)
+    cast = lambda x: torch.from_numpy(x).to(torch.float8_e4m3fn).cuda()   # noqa: E731
+    o, lse = fa.forward_fp8(cast(q), cast(k), cast(v), descales=(1.0, 1.0, 0.5),
+                            scale=float(np.log(2.0)), causal=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to64(o), np.full((B, N, H, d), 0.5)), "O != v_descale for V = 1"
