@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP8_TFLOPS = 5033.2      # 256 CU x 2.4 GHz x 8192 dense e4m3 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention TFLOP/s (bf16 fwd & fwd+bwd, causal) and % of MI355X MFMA peak"
 
@@ -107,6 +108,42 @@ def time_forward_only(fa, torch, B, N, H, d, scale, qk_mult, seed, iters, causal
     del q, k, v, o, lse
     return {"shape_BNHd": [B, N, H, d], "causal": causal, "median_ms": round(med, 4),
             "tflops": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
+
+
+def time_forward_fp8(fa, torch, B, N, H, d, seed, iters, causal=True, qk_mult=1.0):
+    """fa_forward_fp8 on e4m3 inputs (standard normal draws quantised per
+    tensor, the descale mapping max |x| to 448): median call time (the V^T
+    pre-pass and the forward) and its rate against the FP8 matrix peak."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    xs, descales = [], []
+    for mult in (qk_mult, qk_mult, 1.0):
+        x = torch.randn((B, N, H, d), generator=g, device="cuda", dtype=torch.float32) * mult
+        ds = float(x.abs().max()) / 448.0
+        xs.append((x / ds).to(torch.float8_e4m3fn))
+        descales.append(ds)
+        del x
+    q, k, v = xs
+    o = torch.empty((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_forward_fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    scale = d ** -0.5
+    call = lambda: fa.fa_forward_fp8(q, k, v, *descales, o, lse, ws, scale, causal)  # noqa: E731
+    warm_up(call, torch)
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record(st)
+    for i in range(iters):
+        call()
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+    med = ms[len(ms) // 2]
+    tf = fwd_flops(B, H, N, d, causal) / (med * 1e-3) / 1e12
+    del q, k, v, o, lse, ws
+    return {"shape_BNHd": [B, N, H, d], "causal": causal, "median_ms": round(med, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}}
 
 
 def time_decode(fa, torch, B, Nq, Nk, H, d, seed, iters):
@@ -305,6 +342,12 @@ def main():
             "c3_noncausal": time_forward_only(fa, torch, 4, 4096, 16, 128, synth.f32(128 ** -0.5), 1.0, 3, 20,
                                               causal=False),
             "c4": time_forward_only(fa, torch, 1, 32768, 32, 128, synth.f32(128 ** -0.5), 2.0, 4, 10),
+        }
+        log("bench: FP8 (e4m3) forward")
+        result["forward_fp8"] = {
+            "c3_causal": time_forward_fp8(fa, torch, 4, 4096, 16, 128, 3, 20),
+            "c3_noncausal": time_forward_fp8(fa, torch, 4, 4096, 16, 128, 3, 20, causal=False),
+            "c4": time_forward_fp8(fa, torch, 1, 32768, 32, 128, 4, 10, qk_mult=2.0),
         }
         log("bench: split-key decode against a long K/V cache")
         result["decode"] = {
