@@ -8,7 +8,7 @@
     o, lse = forward_fp8(q8, k8, v8, descales=(1, 1, 1), scale=None, causal=False)   # e4m3 inputs
 
 Tensors are contiguous [B, N, H, d] bf16 (or fp32) CUDA tensors with d in
-{64, 128}; lse is fp32 [B, H, N].  scale defaults to d**-0.5, as in the PyTorch
+{64, 128} (bf16 forward and backward also 256); lse is fp32 [B, H, N].  scale defaults to d**-0.5, as in the PyTorch
 module on the page "知识点13 | FlashAttention深度攻略" (blog.xiaohack.org).
 PyTorch only supplies device memory and the current stream: every step runs in
 the HIP kernels of libfa.so.

@@ -17,12 +17,14 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Shape, scale and mask checks shared by every entry point.
-fa_status check_common(int B, int H, int N, int d, float scale, int causal) {
+// Shape, scale and mask checks shared by every entry point.  `wide`: the
+// entry point also has kernels for d = 256 (the bf16 forward and backward);
+// the others take d = 64 and 128 only.
+fa_status check_common(int B, int H, int N, int d, float scale, int causal, bool wide = false) {
   if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && !(wide && d == 256)) return FA_ERR_UNSUPPORTED;
   if (scale < 0.f) return FA_ERR_UNSUPPORTED;
   if (N > (1 << 20)) return FA_ERR_UNSUPPORTED;
   const int64_t bh = (int64_t)B * H;
@@ -64,7 +66,7 @@ extern "C" {
 
 fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
                      int B, int H, int N, int d, float scale, int causal, void* stream) {
-  fa_status st = check_common(B, H, N, d, scale, causal);
+  fa_status st = check_common(B, H, N, d, scale, causal, true);
   if (st == FA_OK) st = check_tensors({Q, K, V, O}, {LSE});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, scale, causal};
@@ -74,8 +76,8 @@ fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float
 fa_status fa_forward_cross(const void* Q, const void* K, const void* V, void* O, float* LSE,
                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
                            void* stream) {
-  fa_status st = check_common(B, H, Nq, d, scale, causal);
-  if (st == FA_OK) st = check_common(B, H, Nk, d, scale, causal);
+  fa_status st = check_common(B, H, Nq, d, scale, causal, true);
+  if (st == FA_OK) st = check_common(B, H, Nk, d, scale, causal, true);
   if (st == FA_OK && causal && Nq > Nk) st = FA_ERR_INVALID_ARG;
   if (st == FA_OK) st = check_tensors({Q, K, V, O}, {LSE});
   if (st != FA_OK) return st;
@@ -119,7 +121,7 @@ fa_status fa_forward_f32(const float* Q, const float* K, const float* V, float* 
 fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                       const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
                       int B, int H, int N, int d, float scale, int causal, void* stream) {
-  fa_status st = check_common(B, H, N, d, scale, causal);
+  fa_status st = check_common(B, H, N, d, scale, causal, true);
   if (st == FA_OK) st = check_tensors({Q, K, V, O, dO, dQ, dK, dV}, {LSE, workspace});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, scale, causal};
@@ -130,8 +132,8 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
 fa_status fa_backward_cross(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                             const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
                             int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream) {
-  fa_status st = check_common(B, H, Nq, d, scale, causal);
-  if (st == FA_OK) st = check_common(B, H, Nk, d, scale, causal);
+  fa_status st = check_common(B, H, Nq, d, scale, causal, true);
+  if (st == FA_OK) st = check_common(B, H, Nk, d, scale, causal, true);
   if (st == FA_OK && causal && Nq > Nk) st = FA_ERR_INVALID_ARG;
   if (st == FA_OK) st = check_tensors({Q, K, V, O, dO, dQ, dK, dV}, {LSE, workspace});
   if (st != FA_OK) return st;
@@ -142,7 +144,7 @@ fa_status fa_backward_cross(const void* Q, const void* K, const void* V, const v
 
 fa_status fa_backward_preprocess(const void* O, const void* dO, const float* LSE, float* workspace,
                                  int B, int H, int N, int d, void* stream) {
-  fa_status st = check_common(B, H, N, d, 1.f, 0);
+  fa_status st = check_common(B, H, N, d, 1.f, 0, true);
   if (st == FA_OK) st = check_tensors({O, dO}, {LSE, workspace});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, 1.f, 0};
@@ -152,7 +154,7 @@ fa_status fa_backward_preprocess(const void* O, const void* dO, const float* LSE
 fa_status fa_backward_dqdkdv(const void* Q, const void* K, const void* V, const void* dO,
                              const float* workspace, void* dQ, void* dK, void* dV,
                              int B, int H, int N, int d, float scale, int causal, void* stream) {
-  fa_status st = check_common(B, H, N, d, scale, causal);
+  fa_status st = check_common(B, H, N, d, scale, causal, true);
   if (st == FA_OK) st = check_tensors({Q, K, V, dO, dQ, dK, dV}, {workspace});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, scale, causal};
@@ -163,7 +165,7 @@ fa_status fa_backward_dqdkdv(const void* Q, const void* K, const void* V, const 
 fa_status fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
                            const float* workspace, void* dK, void* dV,
                            int B, int H, int N, int d, float scale, int causal, void* stream) {
-  fa_status st = check_common(B, H, N, d, scale, causal);
+  fa_status st = check_common(B, H, N, d, scale, causal, true);
   if (st == FA_OK) st = check_tensors({Q, K, V, dO, dK, dV}, {workspace});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, scale, causal};
@@ -174,7 +176,7 @@ fa_status fa_backward_dkdv(const void* Q, const void* K, const void* V, const vo
 fa_status fa_backward_dq(const void* Q, const void* K, const void* V, const void* dO,
                          const float* workspace, void* dQ,
                          int B, int H, int N, int d, float scale, int causal, void* stream) {
-  fa_status st = check_common(B, H, N, d, scale, causal);
+  fa_status st = check_common(B, H, N, d, scale, causal, true);
   if (st == FA_OK) st = check_tensors({Q, K, V, dO, dQ}, {workspace});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, scale, causal};
@@ -218,7 +220,7 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int splits
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
-  if (check_common(B, H, N, d, 1.f, 0) != FA_OK) return 0;
+  if (check_common(B, H, N, d, 1.f, 0, true) != FA_OK) return 0;
   return 2 * (size_t)B * H * N * sizeof(float);
 }
 
@@ -226,7 +228,7 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument (null or misaligned pointer, bad size, scale or mask flag)";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration (head size other than 64/128, negative scale, or size limits)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration (head size without kernels for this entry point, negative scale, or size limits)";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: a HIP launch failed";
     default: return "unknown fa_status";
   }

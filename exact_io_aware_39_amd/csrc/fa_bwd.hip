@@ -480,10 +480,11 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 // Waves per SIMD the dK/dV and fused kernels are compiled for (measured on
 // MI355X).  d = 128 causal: 2 (256 registers, faster than 1); d = 128 without
 // mask: 1 (the dQ tile needs about 280 registers; at 2 the fused kernel
-// spills some 60).
+// spills some 60).  d = 256: 1 (the dK and dV accumulators of a wave alone
+// take 256 registers; a few more spill without the mask).
 template <int D, bool CAUSAL>
 constexpr int bwd_min_waves() {
-  return D == 64 ? (CAUSAL ? 3 : 2) : (CAUSAL ? 2 : 1);
+  return D == 64 ? (CAUSAL ? 3 : 2) : D == 128 ? (CAUSAL ? 2 : 1) : 1;
 }
 
 template <int D, bool CAUSAL>
@@ -629,7 +630,9 @@ BwdArgs make_args(const void* q, const void* k, const void* v, const void* o, co
 hipError_t launch_bwd_pre_bf16(const void* o, const void* dout, const float* lse, float* ws,
                                const AttnShape& s, hipStream_t stream) {
   const BwdArgs a = make_args(nullptr, nullptr, nullptr, o, dout, lse, ws, nullptr, nullptr, nullptr, s);
-  return s.d == 64 ? run_pre<64>(a, s.B, stream) : run_pre<128>(a, s.B, stream);
+  return s.d == 64 ? run_pre<64>(a, s.B, stream)
+         : s.d == 128 ? run_pre<128>(a, s.B, stream)
+                      : run_pre<256>(a, s.B, stream);
 }
 
 hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout,
@@ -638,7 +641,8 @@ hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, con
   const BwdArgs a = make_args(q, k, v, nullptr, dout, nullptr, const_cast<float*>(ws), nullptr, dk, dv, s);
   const int BH = s.B * s.H;
   return s.d == 64 ? run_dkdv<64>(a, BH, s.causal != 0, stream)
-                   : run_dkdv<128>(a, BH, s.causal != 0, stream);
+         : s.d == 128 ? run_dkdv<128>(a, BH, s.causal != 0, stream)
+                      : run_dkdv<256>(a, BH, s.causal != 0, stream);
 }
 
 hipError_t launch_bwd_dqdkdv_bf16(const void* q, const void* k, const void* v, const void* dout,
@@ -647,7 +651,8 @@ hipError_t launch_bwd_dqdkdv_bf16(const void* q, const void* k, const void* v, c
   const BwdArgs a = make_args(q, k, v, nullptr, dout, nullptr, const_cast<float*>(ws), dq, dk, dv, s);
   const int BH = s.B * s.H;
   return s.d == 64 ? run_fused<64>(a, BH, s.causal != 0, stream)
-                   : run_fused<128>(a, BH, s.causal != 0, stream);
+         : s.d == 128 ? run_fused<128>(a, BH, s.causal != 0, stream)
+                      : run_fused<256>(a, BH, s.causal != 0, stream);
 }
 
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout,
@@ -655,7 +660,8 @@ hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const
   const BwdArgs a = make_args(q, k, v, nullptr, dout, nullptr, const_cast<float*>(ws), dq, nullptr, nullptr, s);
   const int BH = s.B * s.H;
   return s.d == 64 ? run_dq<64>(a, BH, s.causal != 0, stream)
-                   : run_dq<128>(a, BH, s.causal != 0, stream);
+         : s.d == 128 ? run_dq<128>(a, BH, s.causal != 0, stream)
+                      : run_dq<256>(a, BH, s.causal != 0, stream);
 }
 
 hipError_t launch_bwd_cross_bf16(const void* q, const void* k, const void* v, const void* o,
@@ -669,9 +675,13 @@ hipError_t launch_bwd_cross_bf16(const void* q, const void* k, const void* v, co
   a.qoff = s.causal ? Nk - s.N : 0;
   const int BH = s.B * s.H;
   const bool causal = s.causal != 0;
-  e = s.d == 64 ? run_dkdv<64>(a, BH, causal, stream) : run_dkdv<128>(a, BH, causal, stream);
+  e = s.d == 64 ? run_dkdv<64>(a, BH, causal, stream)
+         : s.d == 128 ? run_dkdv<128>(a, BH, causal, stream)
+                      : run_dkdv<256>(a, BH, causal, stream);
   if (e != hipSuccess) return e;
-  return s.d == 64 ? run_dq<64>(a, BH, causal, stream) : run_dq<128>(a, BH, causal, stream);
+  return s.d == 64 ? run_dq<64>(a, BH, causal, stream)
+         : s.d == 128 ? run_dq<128>(a, BH, causal, stream)
+                      : run_dq<256>(a, BH, causal, stream);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,

@@ -76,15 +76,16 @@ __device__ __forceinline__ bf16x4 pack_bf16x4(float a0, float a1, float a2, floa
 }
 
 // Per-row chunk permutation for a tile with rows of D bf16 values.
-//  D = 128 (16 chunks, 256 B a row): the 4 low row bits, rotated by 2, so 16
-//    consecutive rows read at one chunk land in 16 different chunk slots, and 4
-//    consecutive rows read over 4 aligned chunks cover 16 different slots.
+//  D = 128 (16 chunks, 256 B a row) and D = 256 (32 chunks, 512 B): the 4 low
+//    row bits, rotated by 2, so 16 consecutive rows read at one chunk land in
+//    16 different chunk slots, and 4 consecutive rows read over 4 aligned
+//    chunks cover 16 different slots.
 //  D = 64 (8 chunks, 128 B a row, two rows per 256 B bank window): rows of one
 //    parity get 8 different slots for rows 0..15, and rows 2 apart differ in
 //    chunk bit 2.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) {
+  if constexpr (D >= 128) {
     return ((row & 3) << 2) | ((row >> 2) & 3);
   } else {
     return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);

@@ -61,12 +61,13 @@ constexpr float kSumLimit = 65536.0f;
 //     cycles for two d = 128 steps.
 template <int D, bool CAUSAL>
 constexpr int fwd_mode() { return D == 128 ? 3 : 0; }
-// Waves per workgroup (32 query rows each) and per SIMD (registers: 168 or
-// 256 VGPRs).
+// Waves per workgroup (32 query rows each) and per SIMD (registers: 168,
+// 256 or, at D = 256, all 512; its four 32 KB K and V buffers also fill the
+// LDS of a CU with one workgroup).
 template <int D, bool CAUSAL>
 constexpr int fwd_wg_waves() { return fwd_mode<D, CAUSAL>() == 3 ? 8 : 4; }
 template <int D>
-constexpr int fwd_waves() { return D == 64 ? 3 : 2; }
+constexpr int fwd_waves() { return D == 64 ? 3 : D == 128 ? 2 : 1; }
 
 // Buffer index carried by a step's buffer tag: the constant of a
 // compile-time tag, 0 for a run-time one (whose offset is in the pointer).
@@ -599,6 +600,7 @@ hipError_t launch_fwd_cross_bf16(const void* q, const void* k, const void* v, vo
   a.c = s.scale * kLog2e;
   const int BH = s.B * s.H;
   if (s.d == 64) return s.causal ? launch<64, true>(a, BH, stream) : launch<64, false>(a, BH, stream);
+  if (s.d == 256) return s.causal ? launch<256, true>(a, BH, stream) : launch<256, false>(a, BH, stream);
   return s.causal ? launch<128, true>(a, BH, stream) : launch<128, false>(a, BH, stream);
 }
 

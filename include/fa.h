@@ -42,9 +42,14 @@
  *                                   aligned, an LSE/workspace pointer not
  *                                   4-byte aligned, B, H or N <= 0, a
  *                                   non-finite scale, causal not 0 or 1;
- *               FA_ERR_UNSUPPORTED  d not 64 or 128, scale < 0, or sizes
- *                                   beyond the limits below; there is no
- *                                   fallback path;
+ *               FA_ERR_UNSUPPORTED  a head size d without kernels (64, 128
+ *                                   and 256 for the bf16 forward and
+ *                                   backward entry points, including the
+ *                                   cross-length ones and the separate
+ *                                   backward passes; 64 and 128 for the
+ *                                   fp32, FP8 and decode ones), scale < 0,
+ *                                   or sizes beyond the limits below; there
+ *                                   is no fallback path;
  *               FA_ERR_LAUNCH       a HIP call or kernel launch failed.
  *             On error nothing has been enqueued.
  *   Limits    N <= 2^20, B*H <= 2^20, H*d <= 2^24, B*N*H*d < 2^40 elements.

@@ -89,8 +89,11 @@ def _bwd(lib, name="fa_backward", ptrs=(P,) * 10, B=1, H=1, N=128, d=64, scale=0
 
 @pytest.mark.parametrize("name", ["fa_forward", "fa_forward_f32"])
 def test_forward_rejects_bad_arguments(lib, name):
-    for d in (0, 32, 96, 256):
+    for d in (0, 32, 96, 512) + ((256,) if name == "fa_forward_f32" else ()):
         assert _fwd(lib, name, d=d) == UNSUPPORTED
+    if name == "fa_forward":
+        # d = 256 passes the head-size check (a null pointer is the first error)
+        assert _fwd(lib, name, d=256, ptrs=(None,) + (P,) * 4) == INVALID
     for B, H, N in ((0, 1, 8), (1, 0, 8), (1, 1, 0), (-1, 1, 8)):
         assert _fwd(lib, name, B=B, H=H, N=N) == INVALID
     assert _fwd(lib, name, N=(1 << 20) + 1) == UNSUPPORTED
@@ -115,6 +118,10 @@ def test_forward_rejects_bad_arguments(lib, name):
 @pytest.mark.parametrize("name", ["fa_backward", "fa_backward_f32"])
 def test_backward_rejects_bad_arguments(lib, name):
     assert _bwd(lib, name, d=80) == UNSUPPORTED
+    if name == "fa_backward":
+        assert _bwd(lib, name, d=256, ptrs=(None,) + (P,) * 9) == INVALID
+    else:
+        assert _bwd(lib, name, d=256) == UNSUPPORTED
     assert _bwd(lib, name, N=0) == INVALID
     assert _bwd(lib, name, scale=float("nan")) == INVALID
     assert _bwd(lib, name, causal=3) == INVALID
@@ -157,6 +164,20 @@ def test_backward_passes_reject_bad_arguments(lib):
             ptrs = [P] * n
             ptrs[i] = P + (2 if i in stats else 8)
             assert fn(*ptrs, 1, 1, 128, 64, 0.1, 1, None) == INVALID
+
+
+def test_head_size_256_only_on_the_bf16_forward_and_backward(lib):
+    assert lib.fa_backward_workspace_bytes(1, 2, 100, 256) == 8 * 2 * 100
+    assert lib.fa_decode_workspace_bytes(1, 2, 1, 100, 256, 0) == 0
+    assert lib.fa_forward_fp8_workspace_bytes(1, 2, 100, 256) == 0
+    assert lib.fa_forward_cross(None, P, P, P, P, 1, 2, 10, 20, 256, 0.1, 1, None) == INVALID
+    assert lib.fa_backward_cross(None, *([P] * 9), 1, 2, 10, 20, 256, 0.1, 1, None) == INVALID
+    for name in ("fa_backward_dqdkdv", "fa_backward_dkdv", "fa_backward_dq"):
+        n = {"fa_backward_dqdkdv": 8, "fa_backward_dkdv": 7, "fa_backward_dq": 6}[name]
+        assert getattr(lib, name)(None, *([P] * (n - 1)), 1, 2, 100, 256, 0.1, 1, None) == INVALID
+    assert lib.fa_backward_preprocess(None, P, P, P, 1, 2, 100, 256, None) == INVALID
+    assert lib.fa_decode(*([P] * 6), 1, 2, 1, 100, 256, 0.1, 1, 0, None) == UNSUPPORTED
+    assert lib.fa_forward_fp8(P, P, P, 1.0, 1.0, 1.0, P, P, P, 1, 2, 10, 20, 256, 0.1, 1, None) == UNSUPPORTED
 
 
 def test_workspace_bytes(lib):

@@ -1,0 +1,66 @@
+"""Head size 256 (bf16): forward, backward and the cross-length entry points
+against the fp64 oracle, under the same bars as d = 64 and 128."""
+import pytest
+import torch
+
+import exact_io_aware_39_amd as fa
+import oracle.attention as ora
+import synth
+from gpu_helpers import check, check_lse, require_gpu, say, to_dev, to64
+from test_gpu_backward import run_and_check as run_backward
+from test_gpu_forward import run_and_check as run_forward
+
+pytestmark = pytest.mark.gpu
+
+D = 256
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 300, 513])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_ragged(N, causal):
+    require_gpu()
+    run_forward((2, N, 2, D), "bf16", 6000 + N, causal, D ** -0.5, tag="d256")
+
+
+@pytest.mark.parametrize("N", [1, 17, 100, 129, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_ragged(N, causal):
+    require_gpu()
+    run_backward((2, N, 2, D), "bf16", 6100 + N, causal, D ** -0.5, tag="d256")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_groups(causal):
+    """B*H a multiple of 8 with a ragged last tile."""
+    require_gpu()
+    run_backward((2, 300, 4, D), "bf16", 6200, causal, D ** -0.5, tag="d256 groups")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_midsize(causal):
+    require_gpu()
+    run_forward((1, 2048, 4, D), "bf16", 6300, causal, D ** -0.5, heads=[(0, 0), (0, 3)], tag="d256 mid")
+    run_backward((1, 2048, 4, D), "bf16", 6301, causal, D ** -0.5, heads=[(0, 1), (0, 2)], tag="d256 mid")
+
+
+@pytest.mark.parametrize("B,Nq,Nk,H,causal", [(1, 100, 300, 2, True), (1, 257, 1000, 2, False),
+                                             (2, 64, 65, 1, True)])
+def test_cross_forward_and_backward(B, Nq, Nk, H, causal):
+    require_gpu()
+    say("d256 cross", B, Nq, Nk, H, causal)
+    host = synth.make_decode_inputs(B, Nq, Nk, H, D, seed=6400 + Nq + Nk, with_do=True)
+    q, k, v, do = (to_dev(host[x]) for x in ("q", "k", "v", "do"))
+    f64 = {x: synth.decode(host[x]) for x in ("q", "k", "v", "do")}
+    scale = synth.f32(D ** -0.5)
+    o, lse = fa.forward_cross(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv = fa.backward_cross(q, k, v, o, do, lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, doh = (f64[x][b, :, h] for x in ("q", "k", "v", "do"))
+            o_ref, lse_ref = ora.decode(qh, kh, vh, scale, causal)
+            check(to64(o[b, :, h]), o_ref, "bf16", f"d256 cross O b={b} h={h}")
+            check_lse(to64(lse[b, h]), lse_ref, f"d256 cross LSE b={b} h={h}")
+            dq_r, dk_r, dv_r, _ = ora.backward_cross(qh, kh, vh, doh, scale, causal)
+            for name, got, ref in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
+                check(to64(got[b, :, h]), ref, "bf16", f"d256 cross {name} b={b} h={h}")
