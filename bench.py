@@ -146,6 +146,38 @@ def time_forward_fp8(fa, torch, B, N, H, d, seed, iters, causal=True, qk_mult=1.
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}}
 
 
+def time_dropout(fa, torch, B, N, H, d, p, iters):
+    """fa_forward_dropout + fa_backward_dropout (causal): median step time and
+    the rate at the FLOPs credited to the plain step (dropout adds none)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8)
+    q, k, v, do = (torch.randn((B, N, H, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device="cuda")
+    scale = d ** -0.5
+
+    def step():
+        fa.fa_forward_dropout(q, k, v, o, lse, scale, True, p, 1234, 0)
+        fa.fa_backward_dropout(q, k, v, o, do, lse, dq, dk, dv, ws, scale, True, p, 1234, 0)
+    warm_up(step, torch)
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record(st)
+    for i in range(iters):
+        step()
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+    med = ms[len(ms) // 2]
+    tf = 3.5 * fwd_flops(B, H, N, d, True) / (med * 1e-3) / 1e12
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    return {"shape_BNHd": [B, N, H, d], "causal": True, "p_drop": p, "median_step_ms": round(med, 4),
+            "tflops_credited": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
+
+
 def time_decode(fa, torch, B, Nq, Nk, H, d, seed, iters):
     """Split-key decode of Nq rows against a [B, Nk, H, d] K/V cache (causal, the
     rows being the last Nq positions): median launch pair (split + merge) time and
@@ -349,6 +381,8 @@ def main():
             "c3_noncausal": time_forward_fp8(fa, torch, 4, 4096, 16, 128, 3, 20, causal=False),
             "c4": time_forward_fp8(fa, torch, 1, 32768, 32, 128, 4, 10, qk_mult=2.0),
         }
+        log("bench: forward + backward with dropout")
+        result["dropout"] = time_dropout(fa, torch, 2, 8192, 16, 64, 0.1, 10)
         log("bench: split-key decode against a long K/V cache")
         result["decode"] = {
             "nq1": time_decode(fa, torch, 8, 1, 32768, 32, 128, 6, 20),

@@ -6,6 +6,8 @@
     dq, dk, dv = backward_cross(q, k, v, o, do, lse, scale=None, causal=False)
     o, lse = decode(q, k, v, scale=None, causal=False, splits=0)   # q: [B, Nq, H, d], Nq <= 32
     o, lse = forward_fp8(q8, k8, v8, descales=(1, 1, 1), scale=None, causal=False)   # e4m3 inputs
+    o, lse = forward_dropout(q, k, v, p_drop, seed, offset=0, scale=None, causal=False)
+    dq, dk, dv = backward_dropout(q, k, v, o, do, lse, p_drop, seed, offset=0, scale=None, causal=False)
 
 Tensors are contiguous [B, N, H, d] bf16 (or fp32) CUDA tensors with d in
 {64, 128} (bf16 forward and backward also 256); lse is fp32 [B, H, N].  scale defaults to d**-0.5, as in the PyTorch
@@ -21,7 +23,8 @@ from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_cross, fa_backwar
                    fa_backward_dq, fa_backward_dqdkdv,
                    fa_backward_preprocess, fa_backward_workspace_bytes, fa_decode,
                    fa_decode_splits, fa_decode_workspace_bytes, fa_forward, fa_forward_cross,
-                   fa_forward_fp8, fa_forward_fp8_workspace_bytes, fa_status_string, load)
+                   fa_forward_fp8, fa_forward_fp8_workspace_bytes, fa_status_string, load,
+                   fa_forward_dropout, fa_backward_dropout)
 
 
 def _scale(q, scale):
@@ -92,3 +95,23 @@ def forward_fp8(q, k, v, descales=(1.0, 1.0, 1.0), scale=None, causal=False, str
     ws = torch.empty(max(1, fa_forward_fp8_workspace_bytes(B, H, Nk, d)), dtype=torch.uint8, device=q.device)
     fa_forward_fp8(q, k, v, *descales, o, lse, ws, _scale(q, scale), causal, stream)
     return o, lse
+
+
+def forward_dropout(q, k, v, p_drop, seed, offset=0, scale=None, causal=False, stream=None):
+    """O and LSE with dropout p_drop on the probabilities (mask from (seed, offset));
+    allocates the outputs."""
+    B, N, H, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_forward_dropout(q, k, v, o, lse, _scale(q, scale), causal, p_drop, seed, offset, stream)
+    return o, lse
+
+
+def backward_dropout(q, k, v, o, do, lse, p_drop, seed, offset=0, scale=None, causal=False, stream=None):
+    """dQ, dK, dV for forward_dropout with the same (p_drop, seed, offset)."""
+    B, N, H, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device=q.device)
+    fa_backward_dropout(q, k, v, o, do, lse, dq, dk, dv, ws, _scale(q, scale), causal, p_drop, seed, offset,
+                        stream)
+    return dq, dk, dv

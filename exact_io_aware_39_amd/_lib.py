@@ -61,6 +61,11 @@ def load() -> ctypes.CDLL:
     lib.fa_decode_splits.restype = I
     lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.fa_decode_workspace_bytes.restype = S
+    U64, U32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.fa_forward_dropout.argtypes = [P] * 5 + [I] * 4 + [F, I, F, U64, U32, P]
+    lib.fa_forward_dropout.restype = I
+    lib.fa_backward_dropout.argtypes = [P] * 10 + [I] * 4 + [F, I, F, U64, U32, P]
+    lib.fa_backward_dropout.restype = I
     lib.fa_forward_fp8.argtypes = [P, P, P, F, F, F, P, P, P, I, I, I, I, I, F, I, P]
     lib.fa_forward_fp8.restype = I
     lib.fa_forward_fp8_workspace_bytes.argtypes = [I, I, I, I]
@@ -259,3 +264,28 @@ def fa_forward_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float
     _call("fa_forward_fp8", load().fa_forward_fp8(
         _ptr(q), _ptr(k), _ptr(v), float(q_descale), float(k_descale), float(v_descale), _ptr(o),
         _ptr(lse), _ptr(workspace), B, H, Nq, Nk, d, float(scale), int(bool(causal)), _stream(stream)))
+
+
+def fa_forward_dropout(q, k, v, o, lse, scale: float, causal: bool, p_drop: float, seed: int, offset: int = 0,
+                       stream=None):
+    """fa_forward_dropout on [B, N, H, d] bf16 tensors; lse [B, H, N] fp32."""
+    B, N, H, d = _shape(q)
+    _check((q, k, v, o), torch.bfloat16)
+    _check((lse,), torch.float32)
+    _call("fa_forward_dropout", load().fa_forward_dropout(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+        float(p_drop), int(seed), int(offset), _stream(stream)))
+
+
+def fa_backward_dropout(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float, causal: bool,
+                        p_drop: float, seed: int, offset: int = 0, stream=None):
+    """fa_backward_dropout on [B, N, H, d] bf16 tensors (the forward's p_drop, seed, offset)."""
+    B, N, H, d = _shape(q)
+    _check((q, k, v, o, do, dq, dk, dv), torch.bfloat16)
+    _check((lse, workspace), torch.float32)
+    if workspace.numel() * 4 < fa_backward_workspace_bytes(B, H, N, d):
+        raise ValueError("workspace smaller than fa_backward_workspace_bytes()")
+    _call("fa_backward_dropout", load().fa_backward_dropout(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), B, H, N, d, float(scale), int(bool(causal)), float(p_drop), int(seed), int(offset),
+        _stream(stream)))

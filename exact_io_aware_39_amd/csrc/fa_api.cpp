@@ -60,6 +60,18 @@ fa_status check_decode(int B, int H, int Nq, int Nk, int d, float scale, int cau
   return FA_OK;
 }
 
+// Keep threshold floor(p 2^32) and scale 1 / (1 - p) of a dropout rate in [0, 1).
+fa::DropParams drop_params(float p, uint64_t seed, uint32_t offset) {
+  fa::DropParams dp;
+  dp.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  dp.key1 = (uint32_t)(seed >> 32);
+  dp.offset = offset;
+  const double t = std::floor((double)p * 4294967296.0);
+  dp.thr = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  dp.inv_keep = (float)(1.0 / (1.0 - (double)p));
+  return dp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -83,6 +95,32 @@ fa_status fa_forward_cross(const void* Q, const void* K, const void* V, void* O,
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, Nq, d, scale, causal};
   return to_status(fa::launch_fwd_cross_bf16(Q, K, V, O, LSE, s, Nk, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_forward_dropout(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             int B, int H, int N, int d, float scale, int causal, float p_drop,
+                             uint64_t seed, uint32_t offset, void* stream) {
+  fa_status st = check_common(B, H, N, d, scale, causal, true);
+  if (st == FA_OK && !(p_drop >= 0.f && p_drop < 1.f)) st = FA_ERR_INVALID_ARG;
+  if (st == FA_OK) st = check_tensors({Q, K, V, O}, {LSE});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal};
+  return to_status(fa::launch_fwd_dropout_bf16(Q, K, V, O, LSE, s, drop_params(p_drop, seed, offset),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_backward_dropout(const void* Q, const void* K, const void* V, const void* O,
+                              const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                              float* workspace, int B, int H, int N, int d, float scale, int causal,
+                              float p_drop, uint64_t seed, uint32_t offset, void* stream) {
+  fa_status st = check_common(B, H, N, d, scale, causal, true);
+  if (st == FA_OK && !(p_drop >= 0.f && p_drop < 1.f)) st = FA_ERR_INVALID_ARG;
+  if (st == FA_OK) st = check_tensors({Q, K, V, O, dO, dQ, dK, dV}, {LSE, workspace});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal};
+  return to_status(fa::launch_bwd_dropout_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, s,
+                                               drop_params(p_drop, seed, offset),
+                                               static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_forward_fp8(const void* Q, const void* K, const void* V, float q_descale,

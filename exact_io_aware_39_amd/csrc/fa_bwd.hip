@@ -56,6 +56,7 @@ struct BwdArgs {
   int64_t bhn;        // B*H*N
   float c;            // scale * log2(e)
   float scale;
+  DropParams drop;    // used by the DROP instantiations only
 };
 
 // ------------------------------------------------------------------ preprocess
@@ -165,7 +166,7 @@ constexpr int dkdv_lds_bytes() {
 }
 
 // dK, dV of key tile kt of head bh (one workgroup).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char* smem) {
   constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
   constexpr int TILE = kBq * RB;            // one Q or dO tile
@@ -258,6 +259,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
       for (int g = 0; g < 2; ++g) {
         const int g4 = 2 * u + g;
         const f32x4 nl = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + (8 * g4 + 4 * hh) * 4);
+        f32x4 nd;
+        if constexpr (DROP) nd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (8 * g4 + 4 * hh) * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
@@ -267,8 +270,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
             const bool hide = qrow >= N || (CAUSAL && mykey > qrow + qoff);
             pv = hide ? 0.f : pv;
           }
-          p[4 * g + e] = pv;
-          ds[4 * g + e] = pv * pacc[r];
+          if constexpr (DROP) {
+            // dV takes P z; dS = P (z dO.V - D) = P (z pacc + (1 - z) (-D))
+            const float z = drop_mult1(a.drop, bh, qi0 + 8 * g4 + 4 * hh + e, mykey);
+            p[4 * g + e] = pv * z;
+            ds[4 * g + e] = pv * __builtin_fmaf(z, pacc[r], (1.f - z) * nd[e]);
+          } else {
+            p[4 * g + e] = pv;
+            ds[4 * g + e] = pv * pacc[r];
+          }
         }
       }
       const bf16x8 pb = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
@@ -340,7 +350,7 @@ constexpr int dq_lds_bytes() {
 }
 
 // dQ of query tile qtile of head bh (one workgroup).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, char* smem) {
   constexpr int NS = 2;   // K and V slots each
   constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
@@ -411,6 +421,12 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float ds[8];
+      float z[2][4];
+      if constexpr (DROP) {
+        // registers 8 u + 4 g + e: keys k0 + 32 j + 8 (2 u + g) + 4 hh + e
+#pragma unroll
+        for (int g = 0; g < 2; ++g) drop_mult4(a.drop, bh, myq, k0 + 32 * j + 8 * (2 * u + g) + 4 * hh, z[g]);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * u + e;
@@ -420,7 +436,12 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
           const bool hide = key >= Nk || (CAUSAL && key > myq + qoff);
           pv = hide ? 0.f : pv;
         }
-        ds[e] = pv * pacc[r];
+        if constexpr (DROP) {
+          const float zz = z[e >> 2][e & 3];
+          ds[e] = pv * __builtin_fmaf(zz, pacc[r], (1.f - zz) * ndval);
+        } else {
+          ds[e] = pv * pacc[r];
+        }
       }
       const bf16x8 db = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
       // dQ^T += K^T dS^T (rows d, columns queries)
@@ -487,20 +508,20 @@ constexpr int bwd_min_waves() {
   return D == 64 ? (CAUSAL ? 3 : 2) : D == 128 ? (CAUSAL ? 2 : 1) : 1;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL>())) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[dkdv_lds_bytes<D>()];
   int bh, kt;
   tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, false, bh, kt);   // low key tiles see the most queries
-  dkdv_tile<D, CAUSAL>(a, bh, kt, smem);
+  dkdv_tile<D, CAUSAL, DROP>(a, bh, kt, smem);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[dq_lds_bytes<D>()];
   int bh, qt;
   tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, true, bh, qt);
-  dq_tile<D, CAUSAL>(a, bh, qt, smem);
+  dq_tile<D, CAUSAL, DROP>(a, bh, qt, smem);
 }
 
 // Both passes in one grid (a.ntiles key tiles and as many query tiles per head,
@@ -553,15 +574,15 @@ __device__ __forceinline__ void fused_task(int id, int nt, int bhcount, bool cau
   bh = group * hpg + pos;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL>())) void bwd_fused_kernel(BwdArgs a) {
   constexpr int LDS = dkdv_lds_bytes<D>() > dq_lds_bytes<D>() ? dkdv_lds_bytes<D>() : dq_lds_bytes<D>();
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   bool is_kv;
   int bh, tile;
   fused_task(blockIdx.x, a.ntiles, a.BH, CAUSAL, is_kv, bh, tile);
-  if (is_kv) dkdv_tile<D, CAUSAL>(a, bh, tile, smem);
-  else dq_tile<D, CAUSAL>(a, bh, tile, smem);
+  if (is_kv) dkdv_tile<D, CAUSAL, DROP>(a, bh, tile, smem);
+  else dq_tile<D, CAUSAL, DROP>(a, bh, tile, smem);
 }
 
 template <int D>
@@ -573,31 +594,31 @@ hipError_t run_pre(const BwdArgs& a, int B, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool DROP = false>
 hipError_t run_dkdv(BwdArgs a, int BH, bool causal, hipStream_t st) {
   a.ntiles = (a.Nk + kKeysPerWg - 1) / kKeysPerWg;
   const dim3 grid(a.ntiles * BH);
-  if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, dim3(256), 0, st, a);
+  if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, DROP>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, DROP>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool DROP = false>
 hipError_t run_dq(BwdArgs a, int BH, bool causal, hipStream_t st) {
   a.ntiles = (a.N + kQPerWg - 1) / kQPerWg;
   const dim3 grid(a.ntiles * BH);
-  if (causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, dim3(256), 0, st, a);
+  if (causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, DROP>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((bwd_dq_kernel<D, false, DROP>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool DROP = false>
 hipError_t run_fused(BwdArgs a, int BH, bool causal, hipStream_t st) {
   // Square attention only (N == Nk): key tiles == query tiles, both 128 rows.
   a.ntiles = (a.N + kKeysPerWg - 1) / kKeysPerWg;
   const dim3 grid(2 * a.ntiles * BH);
-  if (causal) hipLaunchKernelGGL((bwd_fused_kernel<D, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((bwd_fused_kernel<D, false>), grid, dim3(256), 0, st, a);
+  if (causal) hipLaunchKernelGGL((bwd_fused_kernel<D, true, DROP>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((bwd_fused_kernel<D, false, DROP>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -690,6 +711,25 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   hipError_t e = launch_bwd_pre_bf16(o, dout, lse, ws, s, stream);
   if (e != hipSuccess) return e;
   return launch_bwd_dqdkdv_bf16(q, k, v, dout, ws, dq, dk, dv, s, stream);
+}
+
+}  // namespace fa
+
+namespace fa {
+
+hipError_t launch_bwd_dropout_bf16(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                   float* ws, const AttnShape& s, const DropParams& drop,
+                                   hipStream_t stream) {
+  hipError_t e = launch_bwd_pre_bf16(o, dout, lse, ws, s, stream);
+  if (e != hipSuccess) return e;
+  BwdArgs a = make_args(q, k, v, nullptr, dout, nullptr, ws, dq, dk, dv, s);
+  a.drop = drop;
+  const int BH = s.B * s.H;
+  const bool causal = s.causal != 0;
+  return s.d == 64 ? run_fused<64, true>(a, BH, causal, stream)
+         : s.d == 128 ? run_fused<128, true>(a, BH, causal, stream)
+                      : run_fused<256, true>(a, BH, causal, stream);
 }
 
 }  // namespace fa

@@ -20,6 +20,8 @@
 
 #include <type_traits>
 
+#include "fa_launch.hpp"   // DropParams
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -246,6 +248,46 @@ __device__ __forceinline__ void tile_of(int id, int ntiles, int bhcount, bool ca
     rank = L - bh * ntiles;
   }
   tile = heavy_high ? ntiles - 1 - rank : rank;
+}
+
+// ---- dropout on the probabilities
+// The mask is recomputed wherever it is needed, never stored: element (query
+// row i, key j) of head bh uses word j % 4 of Philox4x32-10 (J. K. Salmon et
+// al., "Parallel random numbers: as easy as 1, 2, 3", SC 2011) on the counter
+// (j / 4, i, bh, offset) under the 64-bit seed as key, and is kept when that
+// word is >= thr = floor(p 2^32); a kept probability is scaled by 1 / (1 - p).
+// (DropParams is declared with the launchers.)
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, x0), lo0 = 0xD2511F53u * x0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, x2), lo1 = 0xCD9E8D57u * x2;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return (u32x4){x0, x1, x2, x3};
+}
+
+// Multipliers (0 or 1 / (1 - p)) of keys key4 .. key4 + 3 (key4 % 4 == 0) of
+// query row `row` in head bh: one generator call.
+__device__ __forceinline__ void drop_mult4(const DropParams& dp, int bh, int row, int key4, float (&z)[4]) {
+  const u32x4 w = philox4x32_10((uint32_t)key4 >> 2, (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = w[e] >= dp.thr ? dp.inv_keep : 0.f;
+}
+
+// Multiplier of one element (query row `row`, key `key`) of head bh.
+__device__ __forceinline__ float drop_mult1(const DropParams& dp, int bh, int row, int key) {
+  const u32x4 w = philox4x32_10((uint32_t)key >> 2, (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
+  const int e = key & 3;
+  const uint32_t x = e == 0 ? w[0] : e == 1 ? w[1] : e == 2 ? w[2] : w[3];
+  return x >= dp.thr ? dp.inv_keep : 0.f;
 }
 
 }  // namespace fa

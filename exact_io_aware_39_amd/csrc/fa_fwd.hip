@@ -59,13 +59,14 @@ constexpr float kSumLimit = 65536.0f;
 //     (D = 128).  Waves of one SIMD that share a phase compete for the same
 //     pipe; a probe of the two arrangements measured 3400 against 2100
 //     cycles for two d = 128 steps.
-template <int D, bool CAUSAL>
-constexpr int fwd_mode() { return D == 128 ? 3 : 0; }
+//  With dropout (DROP) every head size takes loop 0.
+template <int D, bool CAUSAL, bool DROP = false>
+constexpr int fwd_mode() { return D == 128 && !DROP ? 3 : 0; }
 // Waves per workgroup (32 query rows each) and per SIMD (registers: 168,
 // 256 or, at D = 256, all 512; its four 32 KB K and V buffers also fill the
 // LDS of a CU with one workgroup).
-template <int D, bool CAUSAL>
-constexpr int fwd_wg_waves() { return fwd_mode<D, CAUSAL>() == 3 ? 8 : 4; }
+template <int D, bool CAUSAL, bool DROP = false>
+constexpr int fwd_wg_waves() { return fwd_mode<D, CAUSAL, DROP>() == 3 ? 8 : 4; }
 template <int D>
 constexpr int fwd_waves() { return D == 64 ? 3 : D == 128 ? 2 : 1; }
 
@@ -87,17 +88,18 @@ struct FwdArgs {
   int Nk;               // key rows per head
   int qoff;             // sequence position of query row 0 (causal: Nk - N)
   float c;   // scale * log2(e)
+  DropParams drop;   // used by the DROP instantiations only
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL>()), fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a) {
+template <int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int KS = D / 16;           // k-steps of the score product
   constexpr int DT = D / 32;           // 32-wide output tiles
   constexpr int RB = D * 2;            // bytes per LDS row (dense, chunks swizzled)
   constexpr int TILE = kBc * RB;       // bytes of one K or V tile
-  constexpr int MODE = fwd_mode<D, CAUSAL>();
-  constexpr int kWaves = fwd_wg_waves<D, CAUSAL>();
+  constexpr int MODE = fwd_mode<D, CAUSAL, DROP>();
+  constexpr int kWaves = fwd_wg_waves<D, CAUSAL, DROP>();
   constexpr int kBr = 32 * kWaves;     // query rows per workgroup
   constexpr int CPW = TILE / 1024 / kWaves;   // 1 KB global->LDS copies per wave per tile
   constexpr int NK = MODE == 3 ? 4 : 2;   // K buffers
@@ -207,7 +209,9 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL>()), fwd_waves<D>()) v
   };
 
   // P = exp2(c S - m_ref) for one step, its row-sum share, and bf16 operands.
-  auto exp_tile = [&](auto mask_tag, const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+  // With dropout the operands carry P times the keep multipliers of the step's
+  // keys (k0 ..), while the row sum takes P itself.
+  auto exp_tile = [&](auto mask_tag, const f32x16 (&s)[2], bf16x8 (&pb)[2][2], int k0) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const float nm = -m_ref;
     float lsum[2] = {0.f, 0.f};
@@ -220,6 +224,16 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL>()), fwd_waves<D>()) v
         if constexpr (MASK) e = (s[j][r] == -INFINITY) ? 0.f : e;
         p[r] = e;
         lsum[r & 1] += e;
+      }
+      if constexpr (DROP) {
+        // registers 4 g .. 4 g + 3: keys k0 + 32 j + 8 g + 4 hh + 0..3
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float z[4];
+          drop_mult4(a.drop, bh, myq, k0 + 32 * j + 8 * g + 4 * hh, z);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[4 * g + e] *= z[e];
+        }
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -257,12 +271,12 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL>()), fwd_waves<D>()) v
       mx = max_halves(mx);
       const float mcand = (mx == -INFINITY) ? -INFINITY : mx * c;
       if (__any(fmaxf(m_ref, mcand) > m_ref + kRescaleLog2)) move_reference(s);
-      lsum = exp_tile(std::true_type{}, s, pb);
+      lsum = exp_tile(std::true_type{}, s, pb, k0);
     } else {
-      lsum = exp_tile(std::false_type{}, s, pb);
+      lsum = exp_tile(std::false_type{}, s, pb, k0);
       if (__any(!(lsum <= kSumLimit))) {
         move_reference(s);
-        lsum = exp_tile(std::false_type{}, s, pb);
+        lsum = exp_tile(std::false_type{}, s, pb, k0);
       }
     }
     l_part += lsum;
@@ -573,20 +587,26 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL>()), fwd_waves<D>()) v
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 hipError_t launch(FwdArgs args, int BH, hipStream_t stream) {
-  constexpr int W = fwd_wg_waves<D, CAUSAL>();
+  constexpr int W = fwd_wg_waves<D, CAUSAL, DROP>();
   args.nqt = (args.N + 32 * W - 1) / (32 * W);
   const int grid = args.nqt * BH;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(64 * W), 0, stream, args);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP>), dim3(grid), dim3(64 * W), 0, stream, args);
   return hipGetLastError();
 }
 
-}  // namespace
+template <bool DROP>
+hipError_t launch_any(const FwdArgs& a, const AttnShape& s, hipStream_t stream) {
+  const int BH = s.B * s.H;
+  if (s.d == 64) return s.causal ? launch<64, true, DROP>(a, BH, stream) : launch<64, false, DROP>(a, BH, stream);
+  if (s.d == 256) return s.causal ? launch<256, true, DROP>(a, BH, stream) : launch<256, false, DROP>(a, BH, stream);
+  return s.causal ? launch<128, true, DROP>(a, BH, stream) : launch<128, false, DROP>(a, BH, stream);
+}
 
-hipError_t launch_fwd_cross_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                                 const AttnShape& s, int Nk, hipStream_t stream) {
-  FwdArgs a;
+FwdArgs make_fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, const AttnShape& s,
+                      int Nk) {
+  FwdArgs a{};
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
   a.v = static_cast<const __bf16*>(v);
@@ -598,10 +618,21 @@ hipError_t launch_fwd_cross_bf16(const void* q, const void* k, const void* v, vo
   a.qoff = s.causal ? Nk - s.N : 0;
   a.BH = s.B * s.H;
   a.c = s.scale * kLog2e;
-  const int BH = s.B * s.H;
-  if (s.d == 64) return s.causal ? launch<64, true>(a, BH, stream) : launch<64, false>(a, BH, stream);
-  if (s.d == 256) return s.causal ? launch<256, true>(a, BH, stream) : launch<256, false>(a, BH, stream);
-  return s.causal ? launch<128, true>(a, BH, stream) : launch<128, false>(a, BH, stream);
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_cross_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const AttnShape& s, int Nk, hipStream_t stream) {
+  return launch_any<false>(make_fwd_args(q, k, v, o, lse, s, Nk), s, stream);
+}
+
+hipError_t launch_fwd_dropout_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   const AttnShape& s, const DropParams& drop, hipStream_t stream) {
+  FwdArgs a = make_fwd_args(q, k, v, o, lse, s, s.N);
+  a.drop = drop;
+  return launch_any<true>(a, s, stream);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -24,6 +24,24 @@ hipError_t launch_fwd_cross_bf16(const void* q, const void* k, const void* v, vo
 size_t fwd_fp8_workspace_bytes(int B, int H, int Nk, int d);
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, float dq, float dk, float dv,
                           void* o, float* lse, void* ws, const AttnShape& s, int Nk, hipStream_t stream);
+// Dropout on the probabilities: element (query row i, key j) of head bh is
+// kept when word j % 4 of Philox4x32-10 on the counter (j / 4, i, bh, offset)
+// under the key (key0, key1) is >= thr; kept probabilities are scaled by
+// inv_keep = 1 / (1 - p).
+struct DropParams {
+  uint32_t key0, key1;   // seed, low and high word
+  uint32_t offset;       // fourth counter word (one mask per offset)
+  uint32_t thr;          // floor(p 2^32)
+  float inv_keep;        // 1 / (1 - p)
+};
+// Forward with dropout (square attention).
+hipError_t launch_fwd_dropout_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   const AttnShape& s, const DropParams& drop, hipStream_t stream);
+// Backward of launch_fwd_dropout_bf16 (same mask), preprocess and the fused passes.
+hipError_t launch_bwd_dropout_bf16(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                   float* ws, const AttnShape& s, const DropParams& drop,
+                                   hipStream_t stream);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           const AttnShape& s, hipStream_t stream);
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,

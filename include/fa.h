@@ -58,6 +58,7 @@
 #define FA_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -91,6 +92,33 @@ fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float
 fa_status fa_forward_cross(const void* Q, const void* K, const void* V, void* O, float* LSE,
                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
                            void* stream);
+
+/*
+ * Forward with dropout on the probabilities, bfloat16 tensors (page "知识点13 |
+ * FlashAttention深度攻略", section 7: the softmax step fused into the one
+ * kernel carries the mask and dropout).  O = (P * Z) V with P the softmax of
+ * scale Q K^T [+ causal mask] and Z_ij = keep_ij / (1 - p_drop); LSE is that
+ * of P (unchanged by dropout).  The mask is never stored: element (query row
+ * i, key j) of head b*H + h is kept when word j % 4 of Philox4x32-10
+ * (Salmon et al., SC 2011) on the counter (j / 4, i, b*H + h, offset) under
+ * the key (seed mod 2^32, seed / 2^32) is >= floor(p_drop 2^32).
+ * 0 <= p_drop < 1 (else FA_ERR_INVALID_ARG); p_drop = 0 keeps everything.
+ * Same layouts, checks and limits as fa_forward (square attention).
+ */
+fa_status fa_forward_dropout(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             int B, int H, int N, int d, float scale, int causal, float p_drop,
+                             uint64_t seed, uint32_t offset, void* stream);
+
+/*
+ * Backward of fa_forward_dropout with the same (p_drop, seed, offset): the
+ * chain rule with the mask replayed, dV = (P * Z)^T dO, dP = (dO V^T) * Z,
+ * D = rowsum(dO * O), dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ * O and LSE are the forward's; same workspace and checks as fa_backward.
+ */
+fa_status fa_backward_dropout(const void* Q, const void* K, const void* V, const void* O,
+                              const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                              float* workspace, int B, int H, int N, int d, float scale, int causal,
+                              float p_drop, uint64_t seed, uint32_t offset, void* stream);
 
 /*
  * Forward on FP8 inputs (page "FlashAttention", part "效果": FlashAttention-3

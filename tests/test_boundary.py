@@ -58,6 +58,11 @@ def lib():
     lib.fa_decode_splits.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i] * 6
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.fa_forward_dropout.argtypes = [vp] * 5 + [i] * 4 + [f, i, f, u64, u32, vp]
+    lib.fa_forward_dropout.restype = i
+    lib.fa_backward_dropout.argtypes = [vp] * 10 + [i] * 4 + [f, i, f, u64, u32, vp]
+    lib.fa_backward_dropout.restype = i
     lib.fa_forward_fp8.argtypes = [vp] * 3 + [f] * 3 + [vp] * 3 + [i] * 5 + [f, i, vp]
     lib.fa_forward_fp8.restype = i
     lib.fa_forward_fp8_workspace_bytes.argtypes = [i] * 4
@@ -71,7 +76,8 @@ def test_header_declares_the_expected_entry_points():
         "fa_backward_preprocess", "fa_backward_dqdkdv", "fa_backward_dkdv", "fa_backward_dq",
         "fa_backward_workspace_bytes", "fa_status_string",
         "fa_decode", "fa_decode_splits", "fa_decode_workspace_bytes", "fa_forward_cross",
-        "fa_backward_cross", "fa_forward_fp8", "fa_forward_fp8_workspace_bytes"])
+        "fa_backward_cross", "fa_forward_fp8", "fa_forward_fp8_workspace_bytes",
+        "fa_forward_dropout", "fa_backward_dropout"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -229,6 +235,31 @@ def test_forward_fp8_rejects_bad_arguments(lib):
         assert call(ptrs=tuple(ptrs)) == INVALID
         ptrs[j] = P + (2 if j == 4 else 8)
         assert call(ptrs=tuple(ptrs)) == INVALID
+
+
+def test_dropout_rejects_bad_arguments(lib):
+    def fwd(p=0.1, d=64, N=100, causal=1, ptrs=(P,) * 5):
+        return lib.fa_forward_dropout(*ptrs, 1, 2, N, d, 0.125, causal, p, 12345, 0, None)
+
+    def bwd(p=0.1, d=64, N=100, causal=1, ptrs=(P,) * 10):
+        return lib.fa_backward_dropout(*ptrs, 1, 2, N, d, 0.125, causal, p, 12345, 0, None)
+    for call in (fwd, bwd):
+        for p in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+            assert call(p=p) == INVALID, p
+        assert call(d=96) == UNSUPPORTED
+        assert call(N=0) == INVALID
+        assert call(causal=2) == INVALID
+    for j in range(5):
+        ptrs = [P] * 5
+        ptrs[j] = None
+        assert fwd(ptrs=tuple(ptrs)) == INVALID
+    for j in range(10):
+        ptrs = [P] * 10
+        ptrs[j] = None
+        assert bwd(ptrs=tuple(ptrs)) == INVALID
+    # p = 0 and d = 256 pass the checks (a null pointer is then the first error)
+    assert fwd(p=0.0, d=256, ptrs=(None,) + (P,) * 4) == INVALID
+    assert bwd(p=0.0, d=256, ptrs=(None,) + (P,) * 9) == INVALID
 
 
 def test_forward_fp8_workspace_bytes(lib):
