@@ -260,7 +260,20 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
         const int g4 = 2 * u + g;
         const f32x4 nl = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + (8 * g4 + 4 * hh) * 4);
         f32x4 nd;
-        if constexpr (DROP) nd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (8 * g4 + 4 * hh) * 4);
+        float zq[4];
+        if constexpr (DROP) {
+          nd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (8 * g4 + 4 * hh) * 4);
+          // lane l32 holds key kw0 + l32 (kw0 % 4 == 0), so each quad holds
+          // four consecutive keys of the same rows.  (At D = 256 the quad
+          // exchange makes this ROCm 7.2 compiler crash in its AGPR rewrite
+          // pass; that head size draws each element on its own.)
+          if constexpr (D <= 128) {
+            drop_mult_quad(a.drop, bh, qi0 + 8 * g4 + 4 * hh, mykey, zq);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zq[e] = drop_mult1(a.drop, bh, qi0 + 8 * g4 + 4 * hh + e, mykey);
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
@@ -272,7 +285,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
           }
           if constexpr (DROP) {
             // dV takes P z; dS = P (z dO.V - D) = P (z pacc + (1 - z) (-D))
-            const float z = drop_mult1(a.drop, bh, qi0 + 8 * g4 + 4 * hh + e, mykey);
+            const float z = zq[e];
             p[4 * g + e] = pv * z;
             ds[4 * g + e] = pv * __builtin_fmaf(z, pacc[r], (1.f - z) * nd[e]);
           } else {

@@ -290,4 +290,24 @@ __device__ __forceinline__ float drop_mult1(const DropParams& dp, int bh, int ro
   return x >= dp.thr ? dp.inv_keep : 0.f;
 }
 
+// Multipliers of rows row0 .. row0 + 3 at this lane's key, for layouts where
+// the four lanes of each DPP quad (lanes 4m .. 4m+3, all active) hold keys
+// 4n .. 4n+3 in lane order and the same four rows.  One generator call per
+// lane instead of four: the lane at quad position q draws the four keys of
+// row row0 + q, the quad pools its 16 keep bits (bit 4 e + j: row e, key j)
+// with two DPP exchanges, and every lane takes bit 4 e + q of each row e.
+__device__ __forceinline__ void drop_mult_quad(const DropParams& dp, int bh, int row0, int key, float (&z)[4]) {
+  const int q = key & 3;
+  const u32x4 w = philox4x32_10((uint32_t)key >> 2, (uint32_t)(row0 + q), (uint32_t)bh, dp.offset, dp.key0, dp.key1);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bits |= (w[j] >= dp.thr ? 1u : 0u) << j;
+  bits <<= 4 * q;
+  // quad_perm [1,0,3,2] then [2,3,0,1]: OR over the four lanes of the quad.
+  bits |= (uint32_t)__builtin_amdgcn_mov_dpp((int)bits, 0xB1, 0xF, 0xF, false);
+  bits |= (uint32_t)__builtin_amdgcn_mov_dpp((int)bits, 0x4E, 0xF, 0xF, false);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = (bits >> (4 * e + q)) & 1u ? dp.inv_keep : 0.f;
+}
+
 }  // namespace fa
