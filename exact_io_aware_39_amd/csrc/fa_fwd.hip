@@ -102,7 +102,11 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), fwd_waves<D
   constexpr int kWaves = fwd_wg_waves<D, CAUSAL, DROP>();
   constexpr int kBr = 32 * kWaves;     // query rows per workgroup
   constexpr int CPW = TILE / 1024 / kWaves;   // 1 KB global->LDS copies per wave per tile
-  constexpr int NK = MODE == 3 ? 4 : 2;   // K buffers
+  // Mode 0 keeps a ring of NB tiles: copies run NB - 1 tiles ahead.  Two
+  // are enough: at D = 64 a ring of three (48 KB of LDS, three workgroups
+  // per CU still fit) measured the same time on MI355X (within 0.5%).
+  constexpr int NB = 2;
+  constexpr int NK = MODE == 3 ? 4 : NB;  // K buffers
   constexpr int NV = NK;                  // V buffers
   __shared__ __attribute__((aligned(1024))) char smem[(NK + NV) * TILE];   // K buffers, then V buffers
 
@@ -514,21 +518,47 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), fwd_waves<D
     if (half == 0) phase_end();
     wait_vmem();              // no copy may land after the workgroup ends
   } else {
-    // Double-buffered K and V of the same tile: step t copies tile t+1 while
-    // it computes scores, softmax and P V of tile t.
+    // A ring of NB buffers for K and NB for V (tile t in buffer t % NB):
+    // step t copies tile t + NB - 1 while it computes scores, softmax and
+    // P V of tile t.  With NB = 3 every step issues one batch of 2 CPW copies
+    // per wave (a tile past the last one is copied from an empty range, which
+    // reads no memory, into a buffer no step reads again), so waiting until
+    // one batch is left in flight completes tile t.  The buffer a step fills
+    // was last read in the step before, which every wave has left at the
+    // step's barrier.
+    auto stage_or_skip = [&](const __bf16* src, int kt, char* dst) __attribute__((always_inline)) {
+      const bool real = kt < nkt;
+      const int rows = real ? min(Nk - kt * kBc, kBc) : 0;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          make_rsrc(src + (int64_t)(real ? kt : 0) * kBc * rs, (uint32_t)(rows * rs * 2));
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, svoff[i], dst + wblk + kWaves * i * 1024);
+    };
     stage_rows(Kg, 0, kbuf);
     stage_rows(Vg, 0, vbuf);
-    // Step kt; `cur_tag` is the buffer holding tile kt (kt & 1), a
-    // compile-time constant in the two-step loops so that the buffer's LDS
+    if constexpr (NB == 3) {
+      stage_or_skip(Kg, 1, kbuf + TILE);
+      stage_or_skip(Vg, 1, vbuf + TILE);
+    }
+    // Step kt; `cur_tag` is the buffer holding tile kt (kt % NB), a
+    // compile-time constant in the unrolled loops so that the buffer's LDS
     // offset is an immediate of every fragment read.
     auto step = [&](int kt, auto mask_tag, auto cur_tag) __attribute__((always_inline)) {
       constexpr bool CT = !std::is_same_v<decltype(cur_tag), int>;
       const int cur = cur_tag;
-      wait_vmem();
-      __syncthreads();
-      if (kt + 1 < nkt) {
-        stage_rows(Kg, kt + 1, kbuf + (cur ^ 1) * TILE);
-        stage_rows(Vg, kt + 1, vbuf + (cur ^ 1) * TILE);
+      if constexpr (NB == 3) {
+        wait_vmem_n<2 * CPW>();
+        __syncthreads();
+        const int nxt = cur == 0 ? 2 : cur - 1;   // (cur + 2) % 3
+        stage_or_skip(Kg, kt + 2, kbuf + nxt * TILE);
+        stage_or_skip(Vg, kt + 2, vbuf + nxt * TILE);
+      } else {
+        wait_vmem();
+        __syncthreads();
+        if (kt + 1 < nkt) {
+          stage_rows(Kg, kt + 1, kbuf + (cur ^ 1) * TILE);
+          stage_rows(Vg, kt + 1, vbuf + (cur ^ 1) * TILE);
+        }
       }
       const int k0 = kt * kBc;
       if (CAUSAL && k0 > qw0 + qoff + 31) return;
@@ -536,37 +566,45 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), fwd_waves<D
       scores(kbuf + cur * TILE, sc);
       const char* vb = CT ? vbuf : vbuf + cur * TILE;
       using Off = std::integral_constant<uint32_t, (uint32_t)(buffer_index<decltype(cur_tag)>() * TILE)>;
-      if constexpr (decltype(mask_tag)::value) {
-        const bool masked = (k0 + kBc > Nk) || (CAUSAL && k0 + kBc - 1 > qw0 + qoff);
-        if (masked) softmax_pv(std::true_type{}, sc, vb, Off{}, k0);
-        else softmax_pv(std::false_type{}, sc, vb, Off{}, k0);
-      } else {
-        softmax_pv(std::false_type{}, sc, vb, Off{}, k0);
-      }
+      softmax_pv(mask_tag, sc, vb, Off{}, k0);
     };
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    if constexpr (CAUSAL) {
-      int kt = 0;
-      for (; kt + 1 < nkt; kt += 2) {
-        step(kt, std::true_type{}, B0{});
-        step(kt + 1, std::true_type{}, B1{});
+    using B2 = std::integral_constant<int, 2>;
+    // Unmasked steps kt .. end - 1 from kt = 0, NB per iteration.
+    auto run_free = [&](int& kt, int end) __attribute__((always_inline)) {
+      if constexpr (NB == 3) {
+        for (; kt + 2 < end; kt += 3) {
+          step(kt, std::false_type{}, B0{});
+          step(kt + 1, std::false_type{}, B1{});
+          step(kt + 2, std::false_type{}, B2{});
+        }
+        if (kt < end) step(kt++, std::false_type{}, B0{});
+        if (kt < end) step(kt++, std::false_type{}, B1{});
+      } else {
+        for (; kt + 1 < end; kt += 2) {
+          step(kt, std::false_type{}, B0{});
+          step(kt + 1, std::false_type{}, B1{});
+        }
+        if (kt < end) step(kt++, std::false_type{}, B0{});
       }
-      if (kt < nkt) step(kt, std::true_type{}, B0{});
+    };
+    int kt = 0;
+    if constexpr (CAUSAL) {
+      // Sections with one softmax path each: first the tiles every key of
+      // which all rows of this wave see (no mask); then the tiles that
+      // straddle the wave's diagonal or the ragged end of the keys (masked),
+      // and the tiles past its diagonal (skipped).
+      run_free(kt, __builtin_amdgcn_readfirstlane(min((qw0 + qoff + 1) / kBc, Nk / kBc)));
     } else {
       // Without a mask only a ragged last tile hides keys, so the loop over
       // the full tiles has a single softmax path.  With the masked path as a
       // branch inside the loop, the compiler kept O in two register sets and
       // copied it twice per step (a fifth of the d = 128 loop's time).
-      const int nfull = Nk / kBc;
-      int kt = 0;
-      for (; kt + 1 < nfull; kt += 2) {
-        step(kt, std::false_type{}, B0{});
-        step(kt + 1, std::false_type{}, B1{});
-      }
-      if (kt < nfull) step(kt++, std::false_type{}, B0{});
-      if (kt < nkt) step(kt, std::true_type{}, kt & 1);
+      run_free(kt, Nk / kBc);
     }
+    for (; kt < nkt; ++kt) step(kt, std::true_type{}, kt % NB);
+    if constexpr (NB == 3) wait_vmem();   // no copy may land after the workgroup ends
   }
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
