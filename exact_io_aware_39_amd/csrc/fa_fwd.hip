@@ -51,8 +51,8 @@ constexpr float kRescaleLog2 = 8.0f;
 constexpr float kSumLimit = 65536.0f;
 // Loop form per instantiation (measured on MI355X):
 //  0  one tile per step: scores, softmax and P V of tile t, 4 waves per
-//     workgroup at 3 waves per SIMD (D = 64: the vector work of a step
-//     exceeds its matrix work, so pairing waves by phase gains little);
+//     workgroup, several workgroups per CU (D = 64: pairing waves by phase
+//     measured slower);
 //  3  ping-pong: 8 waves, two per SIMD in opposite phases; while one wave of
 //     a SIMD runs the products of its step (S(t) and P V of tile t-1) the
 //     other runs the softmax of its tile, and barriers swap the roles
@@ -62,13 +62,16 @@ constexpr float kSumLimit = 65536.0f;
 //  With dropout (DROP) every head size takes loop 0.
 template <int D, bool CAUSAL, bool DROP = false>
 constexpr int fwd_mode() { return D == 128 && !DROP ? 3 : 0; }
-// Waves per workgroup (32 query rows each) and per SIMD (registers: 168,
+// Waves per workgroup (32 query rows each) and per SIMD (registers: 128,
 // 256 or, at D = 256, all 512; its four 32 KB K and V buffers also fill the
-// LDS of a CU with one workgroup).
+// LDS of a CU with one workgroup).  D = 64 runs 4 waves per SIMD: 2% faster
+// on MI355X than 3 (168 registers), although a few loop-invariant values
+// (used after the loop) then go to scratch; with dropout (the generator
+// needs registers) it keeps 3.
 template <int D, bool CAUSAL, bool DROP = false>
 constexpr int fwd_wg_waves() { return fwd_mode<D, CAUSAL, DROP>() == 3 ? 8 : 4; }
-template <int D>
-constexpr int fwd_waves() { return D == 64 ? 3 : D == 128 ? 2 : 1; }
+template <int D, bool DROP>
+constexpr int fwd_waves() { return D == 64 ? (DROP ? 3 : 4) : D == 128 ? 2 : 1; }
 
 // Buffer index carried by a step's buffer tag: the constant of a
 // compile-time tag, 0 for a run-time one (whose offset is in the pointer).
@@ -92,7 +95,7 @@ struct FwdArgs {
 };
 
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), fwd_waves<D>()) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), (fwd_waves<D, DROP>())) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int KS = D / 16;           // k-steps of the score product
   constexpr int DT = D / 32;           // 32-wide output tiles
