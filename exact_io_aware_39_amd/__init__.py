@@ -24,7 +24,8 @@ from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_cross, fa_backwar
                    fa_backward_preprocess, fa_backward_workspace_bytes, fa_decode,
                    fa_decode_splits, fa_decode_workspace_bytes, fa_forward, fa_forward_cross,
                    fa_forward_fp8, fa_forward_fp8_workspace_bytes, fa_status_string, load,
-                   fa_forward_dropout, fa_backward_dropout)
+                   fa_forward_dropout, fa_backward_dropout, fa_backward_single_pass,
+                   fa_backward_single_pass_workspace_bytes)
 
 
 def _scale(q, scale):
@@ -56,6 +57,17 @@ def backward(q, k, v, o, do, lse, scale=None, causal=False, stream=None):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device=q.device)
     fa_backward(q, k, v, o, do, lse, dq, dk, dv, ws, _scale(q, scale), causal, stream)
+    return dq, dk, dv
+
+
+def backward_single_pass(q, k, v, o, do, lse, scale=None, causal=False, stream=None):
+    """dQ, dK, dV of sum(O * dO) by the single-pass backward (dQ accumulated
+    with fp32 atomics); allocates the outputs and the workspace."""
+    B, N, H, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa_backward_single_pass_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32,
+                     device=q.device)
+    fa_backward_single_pass(q, k, v, o, do, lse, dq, dk, dv, ws, _scale(q, scale), causal, stream)
     return dq, dk, dv
 
 

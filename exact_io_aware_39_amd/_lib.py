@@ -50,6 +50,10 @@ def load() -> ctypes.CDLL:
         fn.argtypes = [P] * nptr + [I, I, I, I, F, I, P]
         fn.restype = I
     lib.fa_backward_workspace_bytes.argtypes = [I, I, I, I]
+    lib.fa_backward_single_pass.argtypes = bwd_args
+    lib.fa_backward_single_pass.restype = I
+    lib.fa_backward_single_pass_workspace_bytes.argtypes = [I, I, I, I]
+    lib.fa_backward_single_pass_workspace_bytes.restype = S
     lib.fa_backward_workspace_bytes.restype = S
     lib.fa_forward_cross.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.fa_forward_cross.restype = I
@@ -134,6 +138,24 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float, causal
     _call(name, fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                    _ptr(dv), _ptr(workspace), B, H, N, d, float(scale), int(bool(causal)),
                    _stream(stream)))
+
+
+def fa_backward_single_pass_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load().fa_backward_single_pass_workspace_bytes(B, H, N, d))
+
+
+def fa_backward_single_pass(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float, causal: bool,
+                            stream=None):
+    """fa_backward_single_pass on [B, N, H, d] bf16 tensors (workspace: fp32, at least
+    fa_backward_single_pass_workspace_bytes())."""
+    B, N, H, d = _shape(q)
+    _check((q, k, v, o, do, dq, dk, dv), torch.bfloat16)
+    _check((lse, workspace), torch.float32)
+    if workspace.numel() * 4 < fa_backward_single_pass_workspace_bytes(B, H, N, d):
+        raise ValueError("workspace smaller than fa_backward_single_pass_workspace_bytes()")
+    _call("fa_backward_single_pass", load().fa_backward_single_pass(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), B, H, N, d, float(scale), int(bool(causal)), _stream(stream)))
 
 
 def _check_ws(workspace, B, H, N, d):

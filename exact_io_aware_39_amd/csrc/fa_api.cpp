@@ -257,6 +257,23 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int splits
   return (size_t)B * H * S * Nq * (d + 1) * sizeof(float);
 }
 
+fa_status fa_backward_single_pass(const void* Q, const void* K, const void* V, const void* O,
+                                  const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                                  float* workspace, int B, int H, int N, int d, float scale, int causal,
+                                  void* stream) {
+  fa_status st = check_common(B, H, N, d, scale, causal);
+  if (st == FA_OK) st = check_tensors({Q, K, V, O, dO, dQ, dK, dV, workspace}, {LSE});
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal};
+  return to_status(fa::launch_bwd_single_pass_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, s,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_backward_single_pass_workspace_bytes(int B, int H, int N, int d) {
+  if (check_common(B, H, N, d, 1.f, 0) != FA_OK) return 0;
+  return ((size_t)fa::bwd_single_pass_acc_offset(B, H, N) + (size_t)B * N * H * d) * sizeof(float);
+}
+
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   if (check_common(B, H, N, d, 1.f, 0, true) != FA_OK) return 0;
   return 2 * (size_t)B * H * N * sizeof(float);

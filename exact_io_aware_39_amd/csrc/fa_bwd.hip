@@ -47,6 +47,7 @@ struct BwdArgs {
   const __bf16* dout;
   const float* lse;
   float* ws;          // [-D (B*H*N) | -LSE*log2(e) (B*H*N)]
+  float* dqacc;       // single pass: fp32 dQ / scale, [B, N, H, d] (zeroed before the pass)
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
@@ -162,24 +163,34 @@ constexpr int kKeysPerWg = 128;   // 4 waves x 32 keys
 // batch per 64 rows; the blocks run one after the other in the same
 // registers: 2% faster on MI355X, bitwise the same results), else one.  The
 // dropout pass keeps one (with two it spills).
-template <int D, bool DROP>
-constexpr int dkdv_rows() { return D == 64 && !DROP ? 64 : 32; }
+template <int D, bool DROP, bool ATOMIC = false>
+constexpr int dkdv_rows() { return D == 64 && !DROP && !ATOMIC ? 64 : 32; }
 
-template <int D, bool DROP>
+template <int D, bool DROP, bool ATOMIC = false>
 constexpr int dkdv_lds_bytes() {
-  return 2 * (2 * dkdv_rows<D, DROP>() * D * 2 + 512);
+  return 2 * (2 * dkdv_rows<D, DROP, ATOMIC>() * D * 2 + 512);
 }
 
-// dK, dV of key tile kt of head bh (one workgroup).
-template <int D, bool CAUSAL, bool DROP>
+// Single pass (ATOMIC): LDS per wave for its 32 K rows (a swizzled tile, read
+// transposed as the B operand of dQ += dS K) and for the dS staging of one
+// 32 x 32 block ([query][key] bf16, rows padded to 80 bytes), then the four
+// waves' fp32 dQ partials of the block ([wave][query][d]).
+constexpr int kStRow = 80;
+template <int D>
+constexpr int sp_extra_lds_bytes() { return 4 * (32 * D * 2 + 32 * kStRow) + 4 * 32 * D * 4; }
+
+// dK, dV of key tile kt of head bh (one workgroup).  ATOMIC: also the
+// contribution of these keys to dQ of every query block the tile visits,
+// dQ_blk += dS_blk K (unscaled), added into a.dqacc with fp32 atomics.
+template <int D, bool CAUSAL, bool DROP, bool ATOMIC = false>
 __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char* smem) {
   constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
-  constexpr int kBq = dkdv_rows<D, DROP>(); // query rows per step
+  constexpr int kBq = dkdv_rows<D, DROP, ATOMIC>(); // query rows per step
   constexpr int NSUB = kBq / 32;            // 32-row blocks per step
   constexpr int TILE = kBq * RB;            // one Q or dO tile
   constexpr int CPW = TILE / 1024 / 4;      // 1 KB copies per wave per tile
   constexpr int SLOT = 2 * TILE + 512;      // Q, dO, then 64 floats of -LSE log2 e and of D
-  static_assert(2 * SLOT == dkdv_lds_bytes<D, DROP>(), "LDS layout");
+  static_assert(2 * SLOT == dkdv_lds_bytes<D, DROP, ATOMIC>(), "LDS layout");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -208,6 +219,21 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
   f32x16 dk[DT], dv[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) { dk[t] = (f32x16){}; dv[t] = (f32x16){}; }
+  // Single pass: this wave's K rows as a tile (row l32 = key kw0 + l32) and
+  // its dS^T staging area, after the two slots of the step loop.  The first
+  // step's barrier orders these stores before any read.  Rows of keys past
+  // Nk are zero: their fragments hold a copy of the last key, whose dS is not
+  // zero, and only the zero row keeps them out of dQ.
+  char* const ktile = smem + dkdv_lds_bytes<D, DROP, ATOMIC>() + __builtin_amdgcn_readfirstlane(wave) * (32 * RB);
+  char* const stage_st = smem + dkdv_lds_bytes<D, DROP, ATOMIC>() + 4 * 32 * RB +
+                         __builtin_amdgcn_readfirstlane(wave) * (32 * kStRow);
+  float* const dq_part = reinterpret_cast<float*>(smem + dkdv_lds_bytes<D, DROP, ATOMIC>() + 4 * (32 * RB + 32 * kStRow));
+  f32x16 dqw[DT];   // single pass: this wave's dQ partial of the step's block
+  if constexpr (ATOMIC) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      *reinterpret_cast<bf16x8*>(ktile + tile_off<D>(l32, 2 * ks + hh)) = mykey < Nk ? kf[ks] : (bf16x8){};
+  }
 
   // Under the mask query row i (sequence position i + qoff) sees keys up to
   // i + qoff: the first row that can see key k0 is k0 - qoff.
@@ -312,6 +338,40 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
         dv[t] = mfma32x32x16(tr_frag<D>(slot + TILE, tfb, t, sb, u), pb, dv[t]);
         dk[t] = mfma32x32x16(tr_frag<D>(slot, tfb, t, sb, u), db, dk[t]);
       }
+      if constexpr (ATOMIC) {
+        // dS^T staging: element (query 16u + 8g + 4hh + e, key l32) of the block
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<__bf16*>(stage_st + (16 * u + 8 * g + 4 * hh + e) * kStRow + l32 * 2) = db[4 * g + e];
+      }
+    }
+    if constexpr (ATOMIC) {
+      // dQ (rows queries, columns d) += dS K over this wave's 32 keys: the
+      // staged dS rows are the A operand, and the transposing reads of the K
+      // tile (the A operand of K^T elsewhere) have the B operand's layout.
+      // Lanes of the result then run along d, so each atomic instruction
+      // covers two 128-byte rows of the accumulator.
+      // The staging was written by this wave alone; its LDS accesses complete
+      // in issue order, the asm barrier keeps the compiler from moving the
+      // reads above the writes.
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < DT; ++t) dqw[t] = (f32x16){};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // A operand, lane = query l32: keys 16u + 4hh + 0..3 and 16u + 8 + 4hh + 0..3,
+        // the key order of tr_frag's fragment
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(stage_st + l32 * kStRow + (16 * u + 4 * hh) * 2);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(stage_st + l32 * kStRow + (16 * u + 8 + 4 * hh) * 2);
+        bf16x8 bq;
+        bq[0] = lo[0]; bq[1] = lo[1]; bq[2] = lo[2]; bq[3] = lo[3];
+        bq[4] = hi[0]; bq[5] = hi[1]; bq[6] = hi[2]; bq[7] = hi[3];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) dqw[t] = mfma32x32x16(bq, tr_frag<D>(ktile, tfb, t, 0, u), dqw[t]);
+      }
+      asm volatile("" ::: "memory");
     }
   };
   // One step: publish query tile s, copy tile s+1, then (MODE 1: unmasked,
@@ -323,8 +383,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
     wait_vmem();
     __syncthreads();
     if (s + 1 < nsteps) stage(s + 1, smem + ((s + 1) & 1) * SLOT);
+    const int qi0 = qstart + s * kBq;
     if constexpr (MODE != 0) {
-      const int qi0 = qstart + s * kBq;
 #pragma unroll
       for (int sb = 0; sb < NSUB; ++sb) {
         // masked steps: skip blocks past N or with no row that sees this
@@ -334,6 +394,32 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
         f32x16 sacc, pacc;
         scores(slot, sb, sacc, pacc);
         update(std::bool_constant<MODE == 2>{}, slot, sb, sacc, pacc, qi0 + 32 * sb);
+      }
+    } else if constexpr (ATOMIC) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) dqw[t] = (f32x16){};
+    }
+    if constexpr (ATOMIC) {
+      // The block's dQ partials of the four waves (lane: d = 32 t + l32,
+      // register r: query 8 (r / 4) + 4 hh + r % 4) meet in LDS; wave w sums
+      // query rows 8 w .. 8 w + 7 and adds them to the accumulator, each
+      // atomic instruction covering one row's D contiguous floats.  The next
+      // step's barrier keeps the partials until every wave has read them.
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          dq_part[(wave * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + 32 * t + l32] = dqw[t][r];
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8 * D / 64; ++i) {
+        const int idx = i * 64 + lane;
+        const int row = 8 * wave + idx / D, col = idx % D;
+        const float sum = (dq_part[row * D + col] + dq_part[(32 + row) * D + col]) +
+                          (dq_part[(64 + row) * D + col] + dq_part[(96 + row) * D + col]);
+        if (qi0 + row < N)
+          __hip_atomic_fetch_add(a.dqacc + base + (int64_t)(qi0 + row) * rs + col, sum, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   };
@@ -547,6 +633,33 @@ __global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL>())) void bwd_dkdv_ke
   dkdv_tile<D, CAUSAL, DROP>(a, bh, kt, smem);
 }
 
+// Single-pass backward: the dK/dV tiles also add their share of dQ with fp32
+// atomics (two waves per SIMD at d = 64: the dQ accumulators do not fit
+// beside the pass's registers at three).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_single_pass_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[dkdv_lds_bytes<D, false, true>() + sp_extra_lds_bytes<D>()];
+  int bh, kt;
+  tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, false, bh, kt);
+  dkdv_tile<D, CAUSAL, false, true>(a, bh, kt, smem);
+}
+
+// Zeroes n4 float4s (the single pass's dQ accumulator).
+__global__ __launch_bounds__(256) void zero_f32x4_kernel(f32x4* __restrict__ p, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    p[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
+// dQ = scale * acc, rounded to bf16 (nearest even), 8 elements per thread.
+__global__ __launch_bounds__(256) void dq_from_acc_kernel(const f32x4* __restrict__ acc, __bf16* __restrict__ dq,
+                                                          int64_t n8, float scale) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 x = acc[2 * i], y = acc[2 * i + 1];
+  *reinterpret_cast<bf16x8*>(dq + 8 * i) = pack_bf16x8(x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale,
+                                                       y[0] * scale, y[1] * scale, y[2] * scale, y[3] * scale);
+}
+
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[dq_lds_bytes<D>()];
@@ -742,6 +855,41 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   hipError_t e = launch_bwd_pre_bf16(o, dout, lse, ws, s, stream);
   if (e != hipSuccess) return e;
   return launch_bwd_dqdkdv_bf16(q, k, v, dout, ws, dq, dk, dv, s, stream);
+}
+
+int64_t bwd_single_pass_acc_offset(int B, int H, int N) {
+  return ((2 * (int64_t)B * H * N + 3) / 4) * 4;   // floats; 16-byte aligned
+}
+
+hipError_t launch_bwd_single_pass_bf16(const void* q, const void* k, const void* v, const void* o,
+                                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                       float* ws, const AttnShape& s, hipStream_t stream) {
+  float* acc = ws + bwd_single_pass_acc_offset(s.B, s.H, s.N);
+  const int64_t n = (int64_t)s.B * s.N * s.H * s.d;   // a multiple of 64
+  const int64_t n4 = n / 4;
+  const int64_t zblocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
+  hipLaunchKernelGGL(zero_f32x4_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream, reinterpret_cast<f32x4*>(acc), n4);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_bwd_pre_bf16(o, dout, lse, ws, s, stream);
+  if (e != hipSuccess) return e;
+  BwdArgs a = make_args(q, k, v, nullptr, dout, nullptr, ws, nullptr, dk, dv, s);
+  a.dqacc = acc;
+  a.ntiles = (a.Nk + kKeysPerWg - 1) / kKeysPerWg;
+  const dim3 grid(a.ntiles * a.BH);
+  if (s.d == 64) {
+    if (s.causal) hipLaunchKernelGGL((bwd_single_pass_kernel<64, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_single_pass_kernel<64, false>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (s.causal) hipLaunchKernelGGL((bwd_single_pass_kernel<128, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_single_pass_kernel<128, false>), grid, dim3(256), 0, stream, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(dq_from_acc_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const f32x4*>(acc), static_cast<__bf16*>(dq), n8, s.scale);
+  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -54,6 +54,13 @@ hipError_t launch_bwd_cross_bf16(const void* q, const void* k, const void* v, co
                                  float* ws, const AttnShape& s, int Nk, hipStream_t stream);
 hipError_t launch_bwd_pre_bf16(const void* o, const void* dout, const float* lse, float* ws,
                                const AttnShape& s, hipStream_t stream);
+// Single-pass backward (d = 64, 128): dQ accumulated in fp32 with atomics by
+// the dK/dV pass.  Workspace: [-D | -LSE log2 e | pad to 16 B | dQ acc
+// (B N H d floats)], the accumulator at bwd_single_pass_acc_offset floats.
+int64_t bwd_single_pass_acc_offset(int B, int H, int N);
+hipError_t launch_bwd_single_pass_bf16(const void* q, const void* k, const void* v, const void* o,
+                                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                       float* ws, const AttnShape& s, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout,
                                 const float* ws, void* dk, void* dv, const AttnShape& s,
                                 hipStream_t stream);

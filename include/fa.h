@@ -172,6 +172,31 @@ fa_status fa_backward(const void* Q, const void* K, const void* V, const void* O
                       int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
+ * Single-pass backward, bfloat16 tensors, d = 64 or 128: the same result as
+ * fa_backward (same arguments, layouts and chain rule) computed with one pass
+ * over the key tiles instead of two.  Page "FlashAttention" (the paragraph
+ * after the "效果" table) and page "知识点13 | FlashAttention深度攻略"
+ * (follow-up questions) credit FlashAttention-2 with a different division of
+ * the work across the GPU; this entry point is such a division for the
+ * backward: the dK/dV pass, which already forms dS for its keys, also adds dS K into an
+ * fp32 dQ accumulator with atomic adds (the dQ pass and its recomputation of
+ * S and dP are gone), and a last launch writes dQ = scale * acc as bf16.
+ * The order of the atomic adds varies from run to run, so dQ is reproducible
+ * only to fp32 rounding (dK and dV are bitwise those of fa_backward);
+ * fa_backward stays the deterministic form.  `workspace` is caller-owned
+ * device memory of fa_backward_single_pass_workspace_bytes() bytes, 16-byte
+ * aligned: [-D | -LSE log2 e | padding to 16 bytes | the accumulator
+ * (B*N*H*d floats)]; the call zeroes the accumulator itself.  Same errors as
+ * fa_backward; d = 256 is FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_backward_single_pass(const void* Q, const void* K, const void* V, const void* O,
+                                  const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                                  float* workspace, int B, int H, int N, int d, float scale, int causal,
+                                  void* stream);
+/* Bytes of workspace fa_backward_single_pass needs (0 for invalid sizes). */
+size_t fa_backward_single_pass_workspace_bytes(int B, int H, int N, int d);
+
+/*
  * Backward of fa_forward_cross, bfloat16 tensors: Q, O, dO, dQ are
  * [B, Nq, H, d], K, V, dK, dV [B, Nk, H, d], LSE [B, H, Nq] (the forward's,
  * unchanged).  Masking as in fa_forward_cross (causal = 1: query row i is

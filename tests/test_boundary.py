@@ -58,6 +58,10 @@ def lib():
     lib.fa_decode_splits.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i] * 6
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_backward_single_pass.argtypes = [vp] * 10 + [i] * 4 + [f, i, vp]
+    lib.fa_backward_single_pass.restype = i
+    lib.fa_backward_single_pass_workspace_bytes.argtypes = [i] * 4
+    lib.fa_backward_single_pass_workspace_bytes.restype = ctypes.c_size_t
     u64, u32 = ctypes.c_uint64, ctypes.c_uint32
     lib.fa_forward_dropout.argtypes = [vp] * 5 + [i] * 4 + [f, i, f, u64, u32, vp]
     lib.fa_forward_dropout.restype = i
@@ -77,7 +81,8 @@ def test_header_declares_the_expected_entry_points():
         "fa_backward_workspace_bytes", "fa_status_string",
         "fa_decode", "fa_decode_splits", "fa_decode_workspace_bytes", "fa_forward_cross",
         "fa_backward_cross", "fa_forward_fp8", "fa_forward_fp8_workspace_bytes",
-        "fa_forward_dropout", "fa_backward_dropout"])
+        "fa_forward_dropout", "fa_backward_dropout",
+        "fa_backward_single_pass", "fa_backward_single_pass_workspace_bytes"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -143,6 +148,37 @@ def test_backward_rejects_bad_arguments(lib, name):
         ptrs = [P] * 10
         ptrs[i] = P + 2
         assert _bwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+
+
+def test_single_pass_rejects_bad_arguments(lib):
+    name = "fa_backward_single_pass"
+    assert _bwd(lib, name, d=80) == UNSUPPORTED
+    assert _bwd(lib, name, d=256) == UNSUPPORTED      # d = 64 and 128 only
+    assert _bwd(lib, name, N=0) == INVALID
+    assert _bwd(lib, name, B=-1) == INVALID
+    assert _bwd(lib, name, scale=float("inf")) == INVALID
+    assert _bwd(lib, name, causal=2) == INVALID
+    for i in range(10):
+        ptrs = [P] * 10
+        ptrs[i] = None
+        assert _bwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+    for i in (0, 1, 2, 3, 4, 6, 7, 8, 9):      # tensors and the workspace: 16-byte alignment
+        ptrs = [P] * 10
+        ptrs[i] = P + 4
+        assert _bwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+    ptrs = [P] * 10
+    ptrs[5] = P + 2                             # LSE: 4-byte alignment
+    assert _bwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+
+
+def test_single_pass_workspace_bytes(lib):
+    f = lib.fa_backward_single_pass_workspace_bytes
+    # [-D | -LSE log2 e | padding to 16 bytes | B N H d floats]
+    assert f(2, 16, 8192, 64) == (2 * 2 * 16 * 8192 + 2 * 8192 * 16 * 64) * 4
+    assert f(1, 1, 1, 64) == (4 + 64) * 4
+    assert f(1, 3, 5, 128) == (32 + 3 * 5 * 128) * 4
+    assert f(1, 1, 1, 256) == 0
+    assert f(0, 1, 1, 64) == 0
 
 
 def test_backward_passes_reject_bad_arguments(lib):
