@@ -178,6 +178,42 @@ def time_dropout(fa, torch, B, N, H, d, p, iters):
             "tflops_credited": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
 
 
+def time_single_pass(fa, torch, B, N, H, d, iters):
+    """fa_backward_single_pass (causal; zeroing of the dQ accumulator, the
+    preprocess, the dK/dV pass with atomic dQ, the dQ conversion) against
+    fa_backward on the same inputs: median call times and the backward's
+    credited rate (2.5x the forward's FLOPs)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    q, k, v, do = (torch.randn((B, N, H, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(4))
+    scale = d ** -0.5
+    o, lse = fa.forward(q, k, v, scale=scale, causal=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws1 = torch.empty(fa.fa_backward_single_pass_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32,
+                      device="cuda")
+    ws2 = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device="cuda")
+    calls = {"single_pass": lambda: fa.fa_backward_single_pass(q, k, v, o, do, lse, dq, dk, dv, ws1, scale, True),
+             "two_pass": lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, ws2, scale, True)}
+    out = {"shape_BNHd": [B, N, H, d], "causal": True}
+    st = torch.cuda.current_stream()
+    for name, fn in calls.items():
+        warm_up(fn, torch)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        ev[0].record(st)
+        for i in range(iters):
+            fn()
+            ev[i + 1].record(st)
+        torch.cuda.synchronize()
+        ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+        med = ms[len(ms) // 2]
+        tf = 2.5 * fwd_flops(B, H, N, d, True) / (med * 1e-3) / 1e12
+        out[name] = {"median_ms": round(med, 4), "tflops_credited": round(tf, 1),
+                     "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
+    del q, k, v, do, o, lse, dq, dk, dv, ws1, ws2
+    return out
+
+
 def time_decode(fa, torch, B, Nq, Nk, H, d, seed, iters):
     """Split-key decode of Nq rows against a [B, Nk, H, d] K/V cache (causal, the
     rows being the last Nq positions): median launch pair (split + merge) time and
@@ -383,6 +419,8 @@ def main():
         }
         log("bench: forward + backward with dropout")
         result["dropout"] = time_dropout(fa, torch, 2, 8192, 16, 64, 0.1, 10)
+        log("bench: single-pass backward (atomic dQ) beside the two-pass backward")
+        result["backward_single_pass"] = time_single_pass(fa, torch, 2, 8192, 16, 64, 20)
         log("bench: split-key decode against a long K/V cache")
         result["decode"] = {
             "nq1": time_decode(fa, torch, 8, 1, 32768, 32, 128, 6, 20),
