@@ -297,8 +297,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md on "
-              "sharding); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (heads would shard "
+              "across GPUs with no communication, each running these kernels on its share); "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
