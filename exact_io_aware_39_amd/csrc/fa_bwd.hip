@@ -61,8 +61,10 @@ struct BwdArgs {
 };
 
 // ------------------------------------------------------------------ preprocess
-// CH = D/8 lanes share a row, each reading one 16-byte chunk of O and of dO;
-// the whole [B, N, H, d] tensors are read front to back.
+// CH = D/8 lanes share a row, each reading one 16-byte chunk of O and of dO.
+// Rows go in [B, H, N] order (the order of the outputs), so a workgroup's
+// writes of -D and -LSE log2 e are contiguous and each row read is a whole
+// D*2-byte run (in [B, N, H] order each output word was a line of its own).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ o,
                                                       const __bf16* __restrict__ dout,
@@ -71,10 +73,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
                                                       int64_t rows, int64_t bhn) {
   constexpr int CH = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t r = gid / CH;
+  const int64_t idx = gid / CH;            // output index (b H + h) N + n
   const int ch = (int)(gid % CH);
   float acc = 0.f;
-  if (r < rows) {
+  if (idx < rows) {
+    const int64_t n = idx % N, bh = idx / N;
+    const int64_t h = bh % H, b = bh / H;
+    const int64_t r = (b * N + n) * H + h;  // row of the [B, N, H, d] tensors
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + r * D + ch * 8);
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(dout + r * D + ch * 8);
 #pragma unroll
@@ -82,10 +87,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   }
 #pragma unroll
   for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CH);
-  if (r < rows && ch == 0) {
-    const int64_t h = r % H, bn = r / H;
-    const int64_t n = bn % N, b = bn / N;
-    const int64_t idx = (b * H + h) * N + n;
+  if (idx < rows && ch == 0) {
     ws[idx] = -acc;
     ws[bhn + idx] = -lse[idx] * kLog2e;
   }
