@@ -618,17 +618,19 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 
 // ------------------------------------------------------------------ kernels
 // Waves per SIMD the dK/dV and fused kernels are compiled for (measured on
-// MI355X).  d = 128 causal: 2 (256 registers, faster than 1); d = 128 without
+// MI355X).  d = 64: 3 (168 registers; without the mask five dwords spill,
+// still 3% faster than 2; dropout without the mask keeps 2, where 3 would
+// spill 48).  d = 128 causal: 2 (256 registers, faster than 1); d = 128 without
 // mask: 1 (the dQ tile needs about 280 registers; at 2 the fused kernel
 // spills some 60).  d = 256: 1 (the dK and dV accumulators of a wave alone
 // take 256 registers; a few more spill without the mask).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 constexpr int bwd_min_waves() {
-  return D == 64 ? (CAUSAL ? 3 : 2) : D == 128 ? (CAUSAL ? 2 : 1) : 1;
+  return D == 64 ? (CAUSAL || !DROP ? 3 : 2) : D == 128 ? (CAUSAL ? 2 : 1) : 1;
 }
 
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL>())) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL, DROP>())) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[dkdv_lds_bytes<D, DROP>()];
   int bh, kt;
   tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, false, bh, kt);   // low key tiles see the most queries
@@ -721,7 +723,7 @@ __device__ __forceinline__ void fused_task(int id, int nt, int bhcount, bool cau
 }
 
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL>())) void bwd_fused_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL, DROP>())) void bwd_fused_kernel(BwdArgs a) {
   constexpr int LDS = dkdv_lds_bytes<D, DROP>() > dq_lds_bytes<D>() ? dkdv_lds_bytes<D, DROP>() : dq_lds_bytes<D>();
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   bool is_kv;
