@@ -2,9 +2,18 @@
 
 Bars (per element, GPU value upcast to fp64 minus the oracle's fp64 value):
   fp32 tensors   max |err| <= 1e-5
-  bf16 tensors   max |err| <= 2e-2 and mean |err| <= 2e-3
+  bf16 tensors   |err| <= max(2e-2, ulp_bf16(ref)) per element and
+                 mean |err| <= 2e-3
   LSE            |err| <= 1e-5 * max(1, |LSE|)   (relative, with an absolute
                  floor where LSE is near zero)
+
+ulp_bf16(x) is the spacing of bfloat16 numbers at |x|: 2^(e - 7) for
+2^e <= |x| < 2^(e + 1).  Below |x| = 4 it is at most 2^-6 < 2e-2, so the
+absolute bar of 2e-2 applies unchanged; at |x| >= 4 the two bf16 neighbours of
+the exact value are already 2^-5 = 0.031 apart and rounding the output to the
+nearer one alone may cost 0.0156, so the element is allowed one spacing: half
+for that final rounding, half for the bf16 rounding of the product operands (P,
+dS) before it.  The mean bar is not widened.
 """
 import sys
 
@@ -40,6 +49,19 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def ulp_bf16(x):
+    """Spacing of bfloat16 numbers at |x| (8 significant bits): 2^(e - 7) for
+    2^e <= |x| < 2^(e + 1); the spacing of the smallest normals below them."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.exp2(e - 7.0)
+
+
+def bf16_bar(ref):
+    """Per-element max-error bar for bf16 outputs: max(2e-2, ulp_bf16(ref))."""
+    return np.maximum(BF16_MAX, ulp_bf16(ref))
+
+
 def check(got, ref, dtype, what):
     got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
@@ -48,9 +70,17 @@ def check(got, ref, dtype, what):
     if dtype == "f32":
         assert err.max() <= F32_MAX, f"{what}: max abs err {err.max():.3e} > {F32_MAX}"
     else:
-        assert err.max() <= BF16_MAX, f"{what}: max abs err {err.max():.3e} > {BF16_MAX}"
+        over = err - bf16_bar(ref)
+        i = int(np.argmax(over))
+        assert over.max() <= 0, (f"{what}: abs err {err.flat[i]:.3e} at |ref| = {abs(ref.flat[i]):.3f} "
+                                 f"above its bar {bf16_bar(ref).flat[i]:.3e}")
         assert err.mean() <= BF16_MEAN, f"{what}: mean abs err {err.mean():.3e} > {BF16_MEAN}"
     return float(err.max()), float(err.mean())
+
+
+def count_over(got, ref, bar=BF16_MAX):
+    """Number of elements whose abs error exceeds `bar` (a report, not a check)."""
+    return int((np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64)) > bar).sum())
 
 
 def check_lse(got, ref, what):

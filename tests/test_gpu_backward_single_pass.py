@@ -48,10 +48,8 @@ def run_and_check(shape, seed, causal, scale, heads=None, tag=""):
 @pytest.mark.parametrize("N", [1, 17, 100, 129, 300])
 @pytest.mark.parametrize("causal", [False, True])
 def test_small_ragged(N, d, causal):
-    # The seeds of the two-pass ragged tests: dK and dV are bitwise the
-    # two-pass results.  (With seed 5257 at [2, 129, 2, 128] causal both forms
-    # give one dV element 0.021 from the oracle at |dV| = 5.26, where half a
-    # bf16 ulp alone is 0.0156: the absolute 2e-2 bar, not the kernels.)
+    # The seeds of the two-pass ragged tests (dK and dV are bitwise the
+    # two-pass results); the seed-5257 case of test_gpu_backward runs both forms.
     run_and_check((2, N, 2, d), 3000 + N + d, causal, d ** -0.5, tag="ragged")
 
 
