@@ -6,4 +6,4 @@ definition (materialised S and P); `tile_model` is a CPU model of the blocked
 online-softmax algorithm used to check its recurrence against the definition.
 """
 from .attention import (scores, softmax_rows, forward, forward_rows, backward,  # noqa: F401
-                        forward_bnhd, backward_bnhd)
+                        decode, merge_partials, backward_cross)

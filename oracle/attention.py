@@ -50,7 +50,7 @@ import numpy as np
 
 __all__ = [
     "scores", "softmax_rows", "forward", "forward_rows", "backward",
-    "forward_bnhd", "backward_bnhd", "decode", "merge_partials", "backward_cross",
+    "decode", "merge_partials", "backward_cross",
 ]
 
 
@@ -151,29 +151,3 @@ def backward_cross(q, k, v, do, scale, causal):
     being the last nq positions of the sequence): (dQ, dK, dV, D)."""
     nq, nk = np.shape(q)[0], np.shape(k)[0]
     return backward(q, k, v, do, scale, causal, rows=np.arange(nk - nq, nk))
-
-
-# ----------------------------------------------------------------- [B, N, H, d] helpers
-
-def forward_bnhd(q, k, v, scale, causal, heads=None):
-    """Apply :func:`forward` to each (b, h) of [B, N, H, d] float64 tensors.
-
-    heads: iterable of (b, h) pairs (default: all).  Returns dicts keyed by (b, h).
-    """
-    B, _, H, _ = q.shape
-    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
-    o, lse = {}, {}
-    for b, h in heads:
-        o[(b, h)], lse[(b, h)] = forward(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal)
-    return o, lse
-
-
-def backward_bnhd(q, k, v, do, scale, causal, heads=None):
-    """Apply :func:`backward` to each (b, h); returns dicts of dq, dk, dv, D."""
-    B, _, H, _ = q.shape
-    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
-    res = {"dq": {}, "dk": {}, "dv": {}, "D": {}}
-    for b, h in heads:
-        dq, dk, dv, dvec = backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal)
-        res["dq"][(b, h)], res["dk"][(b, h)], res["dv"][(b, h)], res["D"][(b, h)] = dq, dk, dv, dvec
-    return res

@@ -46,6 +46,15 @@ What is computed (the readings taken, since the pages only name FP8):
     obeys |round_e4m3(y) - y| <= max(2^-4 y, 2^-10) for 0 <= y <= 448,
     whatever maximum p was taken against.
   * round_e4m3 saturates to +-448 (values of p_scale * p never exceed 256).
+  * forward_narrow_accumulator(): forward_quantised_p_online computed the way
+    a kernel whose FP8 matrix instruction sums its k = 64 products in an
+    accumulator of `acc_bits` significant bits would compute it: each block
+    of 64 products (64 of d for the scores, 64 keys for P V) is summed in
+    order with the running sum truncated toward zero to `acc_bits` bits after
+    every addition, and the block's sum is added to a float32 accumulator.
+    AMD does not publish the internal width of that accumulator; this model
+    of an assumed width lets the tests show on the CPU that their error bound
+    covers it.
 """
 from __future__ import annotations
 
@@ -53,8 +62,9 @@ import numpy as np
 
 from .attention import scores, softmax_rows
 
-__all__ = ["E4M3_MAX", "decode_e4m3", "round_e4m3", "e4m3_spacing",
-           "forward", "forward_quantised_p", "forward_quantised_p_online"]
+__all__ = ["E4M3_MAX", "decode_e4m3", "round_e4m3", "e4m3_spacing", "truncate_bits",
+           "forward", "forward_quantised_p", "forward_quantised_p_online",
+           "forward_narrow_accumulator"]
 
 E4M3_MAX = 448.0
 _BIAS = 7
@@ -185,3 +195,65 @@ def forward_quantised_p_online(q8, k8, v8, dq, dk, dv, scale, causal, block=64, 
     o[~live] = 0.0
     lse = np.where(live, m + np.log(np.where(live, l, 1.0)), -np.inf)
     return o, lse, {"x": xs, "p": ps, "pq": pqs, "mref": mref, "m": m, "l": l}
+
+
+def truncate_bits(x, bits):
+    """x rounded toward zero to `bits` significant bits (float64 in and out)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                    # x = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.trunc(m * 2.0 ** bits) / 2.0 ** bits, e)
+
+
+def _narrow_dot_blocks(a, b, acc_bits, kblk=64):
+    """a @ b with the inner dimension taken in blocks of `kblk`: inside a block
+    the products are added one by one to a sum truncated to `acc_bits` bits
+    after each addition; each block's sum is then added to a float32 total."""
+    n = a.shape[1]
+    total = np.zeros((a.shape[0], b.shape[1]), dtype=np.float32)
+    for c0 in range(0, n, kblk):
+        part = np.zeros((a.shape[0], b.shape[1]))
+        for c in range(c0, min(c0 + kblk, n)):
+            part = truncate_bits(part + a[:, c:c + 1] * b[c:c + 1, :], acc_bits)
+        total = (total + part.astype(np.float32)).astype(np.float32)
+    return total.astype(np.float64)
+
+
+def forward_narrow_accumulator(q8, k8, v8, dq, dk, dv, scale, causal, acc_bits=16, block=64,
+                               p_scale=256.0):
+    """The rounded-P online forward with both products summed through a narrow
+    accumulator of `acc_bits` bits (see the module notes): returns (O, LSE).
+
+    Scores: the code values of Q and K (products of two e4m3 values are exact)
+    summed per 64 of d, then multiplied by scale * dq * dk in float32.  P V:
+    the e4m3 values of 2^8 p against the running maximum of each block of
+    `block` keys, times the code values of V, summed per 64 keys.
+    """
+    q, k, v = _decoded(q8, k8, v8)
+    nq, nk = q.shape[0], k.shape[0]
+    rows = np.arange(nk - nq, nk)
+    raw = _narrow_dot_blocks(q, k.T, acc_bits)
+    s32 = (raw.astype(np.float32) * np.float32(float(scale) * float(dq) * float(dk))).astype(np.float32)
+    if causal:
+        s32 = np.where(np.arange(nk)[None, :] > rows[:, None], np.float32(-np.inf), s32)
+    m = np.full(nq, -np.inf)
+    l = np.zeros(nq)
+    acc = np.zeros((nq, v.shape[1]))
+    for j0 in range(0, nk, block):
+        sb = s32[:, j0:j0 + block]
+        m_new = np.maximum(m, sb.max(axis=1).astype(np.float64))
+        grow = np.isfinite(m_new)
+        alpha = np.where(grow & np.isfinite(m), np.exp(np.where(grow, m - m_new, 0.0)), 0.0)
+        acc *= alpha[:, None]
+        l *= alpha
+        m = m_new
+        m32 = np.where(grow, m, 0.0).astype(np.float32)[:, None]
+        p = np.exp((sb - m32).astype(np.float32)).astype(np.float32)
+        pq = round_e4m3(np.float64(p_scale) * p.astype(np.float64))
+        acc += _narrow_dot_blocks(pq, v[j0:j0 + block], acc_bits)
+        l += p.astype(np.float64).sum(axis=1)
+    live = np.isfinite(m)
+    denom = np.where(live, p_scale * l, 1.0)
+    o = acc * float(dv) / denom[:, None]
+    o[~live] = 0.0
+    lse = np.where(live, m + np.log(np.where(live, l, 1.0)), -np.inf)
+    return o, lse

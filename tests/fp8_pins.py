@@ -29,6 +29,15 @@ bound that follows from the format:
   * On random inputs the rounded-P results (both variants) lie within the bound
     dv sum_j max(2^-4 y_ij, 2^-10) |V_j| / (256 l_i), y = 256 p, of the exact
     one, and the bound is not met trivially (the two differ).
+  * truncate_bits keeps the leading bits of the binary expansion: 1.9999 to 2
+    bits is 1.5, -5.5 to 2 bits is -4, 3 to 2 bits stays 3, and to 24 bits it
+    agrees with numpy's float32 conversion wherever that rounds down in
+    magnitude.
+  * The narrow-accumulator model with a 53-bit accumulator is the online
+    rounded-P result (up to the float32 totals); with integer-coded Q and K of
+    magnitude <= 15 and a 15-bit accumulator every score is an exact integer
+    sum, so it equals the 53-bit model; with an 8-bit accumulator on spread
+    inputs it differs.
 """
 from __future__ import annotations
 
@@ -214,8 +223,43 @@ def pin_online_worked_three_keys(fp8):
     assert np.array_equal(aux_f["pq"][0], [80.0, 24.0, 256.0]), f"final-maximum Pq = {aux_f['pq'][0]}"
 
 
+def pin_truncate_bits(fp8):
+    got = fp8.truncate_bits(np.array([1.9999, -5.5, 3.0, 0.0, 1.0]), 2)
+    assert np.array_equal(got, [1.5, -4.0, 3.0, 0.0, 1.0]), f"truncate_bits to 2 bits: {got}"
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(10000) * np.exp2(rng.integers(-20, 20, 10000))
+    f = x.astype(np.float32).astype(np.float64)
+    down = np.abs(f) <= np.abs(x)
+    assert np.array_equal(fp8.truncate_bits(x, 24)[down], f[down]), "truncate_bits(24) vs float32"
+    assert (np.abs(fp8.truncate_bits(x, 24)) <= np.abs(x)).all(), "truncation must not grow |x|"
+
+
+def pin_narrow_accumulator(fp8):
+    rng = np.random.default_rng(23)
+    nq, nk, d = 40, 150, 128
+    q = _codes(rng.standard_normal((nq, d)).astype(np.float32) * 4)
+    k = _codes(rng.standard_normal((nk, d)).astype(np.float32) * 4)
+    v = _codes(rng.standard_normal((nk, d)).astype(np.float32))
+    sc = 0.01
+    for causal in (False, True):
+        o53, lse53 = fp8.forward_narrow_accumulator(q, k, v, 1.0, 1.0, 1.0, sc, causal, acc_bits=53)
+        o_on, lse_on, _ = fp8.forward_quantised_p_online(q, k, v, 1.0, 1.0, 1.0, sc, causal, block=64)
+        _close(o53, o_on, 2e-4, "53-bit accumulator = online rounded-P O")
+        _close(lse53, lse_on, 1e-5, "53-bit accumulator = online rounded-P LSE")
+        o8, _ = fp8.forward_narrow_accumulator(q, k, v, 1.0, 1.0, 1.0, sc, causal, acc_bits=8)
+        assert np.abs(o8 - o53).max() > 1e-3, "an 8-bit accumulator should change O"
+    qi = _codes(np.clip(np.rint(rng.standard_normal((nq, d)) * 4), -15, 15).astype(np.float32))
+    ki = _codes(np.clip(np.rint(rng.standard_normal((nk, d)) * 4), -15, 15).astype(np.float32))
+    for causal in (False, True):
+        o15, lse15 = fp8.forward_narrow_accumulator(qi, ki, v, 0.25, 0.25, 1.0, sc, causal, acc_bits=15)
+        o53, lse53 = fp8.forward_narrow_accumulator(qi, ki, v, 0.25, 0.25, 1.0, sc, causal, acc_bits=53)
+        # scores exact either way; the P V sums may differ by the 15-bit rounding
+        _close(lse15, lse53, 0.0, "integer scores with a 15-bit accumulator")
+        _close(o15, o53, 2e-3, "integer scores with a 15-bit accumulator, O")
+
+
 FP8_PINS = [
     pin_decode, pin_round, pin_zero_query, pin_descales, pin_exact_powers_of_two,
     pin_worked_two_keys, pin_online_matches_final_max, pin_online_worked_three_keys,
-    pin_rounding_bound,
+    pin_rounding_bound, pin_truncate_bits, pin_narrow_accumulator,
 ]

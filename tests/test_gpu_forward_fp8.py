@@ -1,10 +1,12 @@
 """GPU parity of fa_forward_fp8 (e4m3 Q, K, V with per-tensor descales).
 
-Each head is compared with the FP8 oracles of oracle/fp8.py under the bounds of
-tests/fp8_bounds.py: every row against the exact attention of the dequantised
-inputs (forward) within the rounding bound, and, for inputs whose Q and K are
-integer-coded (exact scores), every row against the online rounded-P oracle
-(forward_quantised_p_online, 64-key blocks) within the tight bound.
+Each head is compared with the exact attention of the dequantised inputs
+(oracle/fp8.py forward) under the bound of tests/fp8_bounds.py, whose
+constants come from the OCP E4M3 format, the round-to-nearest-even conversion
+and a stated assumption on the matrix instruction's accumulator width.  For
+integer-coded Q and K the distance to the online rounded-P model with the
+kernel's 64-key blocks (forward_quantised_p_online) is printed as a
+diagnostic; it gates nothing.
 """
 import numpy as np
 import pytest
@@ -40,25 +42,24 @@ def _dev(x):
 
 
 def _check_rows(o, lse, q8, k8, v8, descales, scale, causal, exact, what):
-    """Bounds for one head (o: [nq, d], lse: [nq]); returns the largest
-    error-to-bound ratios (loose, tight) and the number of ambiguous p."""
+    """The bound for one head (o: [nq, d], lse: [nq]); returns the largest
+    error-to-bound ratio, and (diagnostic, integer-coded Q and K only) the
+    largest ratio to the tight bound against the 64-key online model and the
+    number of ambiguous p."""
     assert np.isfinite(o).all() and np.isfinite(lse).all(), f"{what}: non-finite output"
     o_ex, lse_ex = fp8.forward(q8, k8, v8, *descales, scale, causal)
-    lb = loose_bound(q8, k8, v8, descales, scale, causal, o_ex, exact)
+    lb = loose_bound(q8, k8, v8, descales, scale, causal, o_ex)
     err = np.abs(o - o_ex)
     assert (err <= lb).all(), (f"{what}: O outside the rounding bound by "
                                f"{(err - lb).max():.3e} (max err {err.max():.3e})")
     lerr = np.abs(lse - lse_ex)
-    assert (lerr <= lse_bound(q8, k8, descales, scale, causal, lse_ex, exact)).all(), \
+    assert (lerr <= lse_bound(q8, k8, descales, scale, causal, lse_ex)).all(), \
         f"{what}: LSE err {lerr.max():.3e} above its bound"
     ratio_tight, namb = 0.0, 0
-    if exact:
+    if exact:   # diagnostic, not a gate
         o_on, _, aux = fp8.forward_quantised_p_online(q8, k8, v8, *descales, scale, causal, block=64)
-        tb, namb = tight_bound(q8, k8, v8, descales, scale, causal, o_on, aux, True)
-        terr = np.abs(o - o_on)
-        assert (terr <= tb).all(), (f"{what}: O differs from the online rounded-P oracle by "
-                                    f"{terr.max():.3e}, {(terr - tb).max():.3e} above the tight bound")
-        ratio_tight = float((terr / tb).max())
+        tb, namb = tight_bound(q8, k8, v8, descales, scale, causal, o_on, aux)
+        ratio_tight = float((np.abs(o - o_on) / tb).max())
     return float((err / lb).max()), ratio_tight, namb
 
 
@@ -79,7 +80,8 @@ def test_forward_fp8_matches_oracles(B, Nq, Nk, H, d, causal, qk_int):
             r = _check_rows(o64[b, :, h], lse64[b, h], host["q"][b, :, h], host["k"][b, :, h],
                             host["v"][b, :, h], descales, scale, causal, qk_int, f"(b={b}, h={h})")
             worst = [max(worst[0], r[0]), max(worst[1], r[1]), worst[2] + r[2]]
-    say(f"  error / bound: loose {worst[0]:.3f}, tight {worst[1]:.3f}; ambiguous p {worst[2]}")
+    say(f"  error / bound {worst[0]:.3f}; diagnostic: error / tight bound of the 64-key model "
+        f"{worst[1]:.3f}, ambiguous p {worst[2]}")
 
 
 def test_forward_fp8_full_size_sampled_rows():

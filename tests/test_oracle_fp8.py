@@ -119,3 +119,43 @@ def test_fp8_unmutated_online_template_passes(monkeypatch):
     monkeypatch.setattr(fp8, "forward_quantised_p_online", _online_variant("none"))
     for pin in FP8_PINS:
         pin(fp8)
+
+
+# The FP8 GPU parity bound (tests/fp8_bounds.py) rests on an assumed minimum
+# accumulator width of the FP8 matrix instruction.  A model of a kernel with
+# exactly that width (truncating after every addition) must stay inside the
+# bound, and a model with a much narrower accumulator must not, so that the
+# bound is shown to cover the assumption without being vacuous.
+_ACC_CASES = [   # Nq, Nk, d, causal, integer-coded Q and K
+    (256, 256, 64, True, True),
+    (200, 333, 128, False, False),
+    (300, 300, 128, True, False),
+    (500, 200, 64, False, True),
+    (1, 1, 64, False, True),
+]
+
+
+def _acc_ratios(acc_bits):
+    import synth
+    from fp8_bounds import loose_bound, lse_bound
+    worst = 0.0
+    for Nq, Nk, d, causal, qi in _ACC_CASES:
+        host = synth.make_fp8_inputs(1, Nq, Nk, 1, d, seed=3000 + Nq + 7 * Nk + d, qk_int=qi)
+        q8, k8, v8 = (host[x][0, :, 0] for x in "qkv")
+        ds = host["descales"]
+        sc = synth.f32(d ** -0.5)
+        o_ex, lse_ex = fp8.forward(q8, k8, v8, *ds, sc, causal)
+        o_m, lse_m = fp8.forward_narrow_accumulator(q8, k8, v8, *ds, sc, causal, acc_bits=acc_bits)
+        r_o = float((np.abs(o_m - o_ex) / loose_bound(q8, k8, v8, ds, sc, causal, o_ex)).max())
+        r_l = float((np.abs(lse_m - lse_ex) / lse_bound(q8, k8, ds, sc, causal, lse_ex)).max())
+        worst = max(worst, r_o, r_l)
+    return worst
+
+
+def test_bound_covers_assumed_accumulator():
+    from fp8_bounds import ACC_BITS
+    assert _acc_ratios(ACC_BITS) <= 1.0
+
+
+def test_bound_rejects_8_bit_accumulator():
+    assert _acc_ratios(8) > 1.0
