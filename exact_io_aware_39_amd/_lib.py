@@ -108,6 +108,22 @@ def _check(ts, dtype):
     for t in ts:
         if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
             raise ValueError(f"expected contiguous {dtype} CUDA tensors, got {t.dtype} on {t.device}")
+    devs = {t.device for t in ts}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(map(str, devs))}")
+
+
+def _same_shape(where, ref, named):
+    """Every tensor of `named` ({name: tensor}) must have the shape of `ref`."""
+    want = tuple(ref.shape)
+    for name, t in named.items():
+        if tuple(t.shape) != want:
+            raise ValueError(f"{where}: {name} has shape {tuple(t.shape)}, expected {want}")
+
+
+def _lse_shape(where, lse, B, H, N, name="lse"):
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"{where}: {name} has shape {tuple(lse.shape)}, expected [B, H, N] = {(B, H, N)}")
 
 
 def _call(name, status):
@@ -119,6 +135,8 @@ def fa_forward(q, k, v, o, lse, scale: float, causal: bool, stream=None):
     """fa_forward / fa_forward_f32 on [B, N, H, d] tensors (bf16 or fp32)."""
     B, N, H, d = _shape(q)
     name = "fa_forward" if q.dtype == torch.bfloat16 else "fa_forward_f32"
+    _same_shape(name, q, {"k": k, "v": v, "o": o})
+    _lse_shape(name, lse, B, H, N)
     _check((q, k, v, o), q.dtype)
     _check((lse,), torch.float32)
     fn = getattr(load(), name)
@@ -130,6 +148,8 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float, causal
     """fa_backward / fa_backward_f32 on [B, N, H, d] tensors (bf16 or fp32)."""
     B, N, H, d = _shape(q)
     name = "fa_backward" if q.dtype == torch.bfloat16 else "fa_backward_f32"
+    _same_shape(name, q, {"k": k, "v": v, "o": o, "do": do, "dq": dq, "dk": dk, "dv": dv})
+    _lse_shape(name, lse, B, H, N)
     _check((q, k, v, o, do, dq, dk, dv), q.dtype)
     _check((lse, workspace), torch.float32)
     if workspace.numel() * 4 < fa_backward_workspace_bytes(B, H, N, d):
@@ -149,6 +169,8 @@ def fa_backward_single_pass(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: f
     """fa_backward_single_pass on [B, N, H, d] bf16 tensors (workspace: fp32, at least
     fa_backward_single_pass_workspace_bytes())."""
     B, N, H, d = _shape(q)
+    _same_shape("fa_backward_single_pass", q, {"k": k, "v": v, "o": o, "do": do, "dq": dq, "dk": dk, "dv": dv})
+    _lse_shape("fa_backward_single_pass", lse, B, H, N)
     _check((q, k, v, o, do, dq, dk, dv), torch.bfloat16)
     _check((lse, workspace), torch.float32)
     if workspace.numel() * 4 < fa_backward_single_pass_workspace_bytes(B, H, N, d):
@@ -166,6 +188,8 @@ def _check_ws(workspace, B, H, N, d):
 def fa_backward_preprocess(o, do, lse, workspace, stream=None):
     """fa_backward_preprocess: workspace = [-D = -rowsum(dO * O) | -LSE log2(e)] (bf16 tensors)."""
     B, N, H, d = _shape(o)
+    _same_shape("fa_backward_preprocess", o, {"do": do})
+    _lse_shape("fa_backward_preprocess", lse, B, H, N)
     _check((o, do), torch.bfloat16)
     _check((lse, workspace), torch.float32)
     _check_ws(workspace, B, H, N, d)
@@ -176,6 +200,7 @@ def fa_backward_preprocess(o, do, lse, workspace, stream=None):
 def fa_backward_dqdkdv(q, k, v, do, workspace, dq, dk, dv, scale: float, causal: bool, stream=None):
     """fa_backward_dqdkdv: dQ, dK and dV in one launch from the preprocessed workspace."""
     B, N, H, d = _shape(q)
+    _same_shape("fa_backward_dqdkdv", q, {"k": k, "v": v, "do": do, "dq": dq, "dk": dk, "dv": dv})
     _check((q, k, v, do, dq, dk, dv), torch.bfloat16)
     _check((workspace,), torch.float32)
     _check_ws(workspace, B, H, N, d)
@@ -187,6 +212,7 @@ def fa_backward_dqdkdv(q, k, v, do, workspace, dq, dk, dv, scale: float, causal:
 def fa_backward_dkdv(q, k, v, do, workspace, dk, dv, scale: float, causal: bool, stream=None):
     """fa_backward_dkdv: dK and dV from the preprocessed workspace (bf16 tensors)."""
     B, N, H, d = _shape(q)
+    _same_shape("fa_backward_dkdv", q, {"k": k, "v": v, "do": do, "dk": dk, "dv": dv})
     _check((q, k, v, do, dk, dv), torch.bfloat16)
     _check((workspace,), torch.float32)
     _check_ws(workspace, B, H, N, d)
@@ -198,6 +224,7 @@ def fa_backward_dkdv(q, k, v, do, workspace, dk, dv, scale: float, causal: bool,
 def fa_backward_dq(q, k, v, do, workspace, dq, scale: float, causal: bool, stream=None):
     """fa_backward_dq: dQ from the preprocessed workspace (bf16 tensors)."""
     B, N, H, d = _shape(q)
+    _same_shape("fa_backward_dq", q, {"k": k, "v": v, "do": do, "dq": dq})
     _check((q, k, v, do, dq), torch.bfloat16)
     _check((workspace,), torch.float32)
     _check_ws(workspace, B, H, N, d)
@@ -220,6 +247,7 @@ def fa_decode(q, k, v, o, lse, workspace, scale: float, causal: bool, splits: in
     Bk, Nk, Hk, dk = _shape(k)
     if (Bk, Hk, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape):
         raise ValueError("fa_decode: q/o and k/v must share B, H and d, k and v the same shape")
+    _lse_shape("fa_decode", lse, B, H, Nq)
     _check((q, k, v, o), torch.bfloat16)
     _check((lse, workspace), torch.float32)
     if workspace.numel() * 4 < fa_decode_workspace_bytes(B, H, Nq, Nk, d, splits):
@@ -237,6 +265,7 @@ def fa_backward_cross(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float, 
     if (Bk, Hk, dk_) != (B, H, d) or any(tuple(t.shape) != tuple(k.shape) for t in (v, dk, dv)) \
             or any(tuple(t.shape) != tuple(q.shape) for t in (o, do, dq)):
         raise ValueError("fa_backward_cross: q/o/do/dq and k/v/dk/dv must share B, H and d")
+    _lse_shape("fa_backward_cross", lse, B, H, Nq)
     _check((q, k, v, o, do, dq, dk, dv), torch.bfloat16)
     _check((lse, workspace), torch.float32)
     if workspace.numel() * 4 < fa_backward_workspace_bytes(B, H, Nq, d):
@@ -252,6 +281,7 @@ def fa_forward_cross(q, k, v, o, lse, scale: float, causal: bool, stream=None):
     Bk, Nk, Hk, dk = _shape(k)
     if (Bk, Hk, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape):
         raise ValueError("fa_forward_cross: q/o and k/v must share B, H and d, k and v the same shape")
+    _lse_shape("fa_forward_cross", lse, B, H, Nq)
     _check((q, k, v, o), torch.bfloat16)
     _check((lse,), torch.float32)
     _call("fa_forward_cross", load().fa_forward_cross(
@@ -274,6 +304,7 @@ def fa_forward_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float
     Bk, Nk, Hk, dk = _shape(k)
     if (Bk, Hk, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape):
         raise ValueError("fa_forward_fp8: q/o and k/v must share B, H and d, k and v the same shape")
+    _lse_shape("fa_forward_fp8", lse, B, H, Nq)
     for t in (q, k, v):
         if not t.is_cuda or t.dtype not in _E4M3_DTYPES or not t.is_contiguous():
             raise ValueError(f"fa_forward_fp8: expected contiguous e4m3 CUDA tensors, got {t.dtype} on {t.device}")
@@ -292,6 +323,8 @@ def fa_forward_dropout(q, k, v, o, lse, scale: float, causal: bool, p_drop: floa
                        stream=None):
     """fa_forward_dropout on [B, N, H, d] bf16 tensors; lse [B, H, N] fp32."""
     B, N, H, d = _shape(q)
+    _same_shape("fa_forward_dropout", q, {"k": k, "v": v, "o": o})
+    _lse_shape("fa_forward_dropout", lse, B, H, N)
     _check((q, k, v, o), torch.bfloat16)
     _check((lse,), torch.float32)
     _call("fa_forward_dropout", load().fa_forward_dropout(
@@ -303,6 +336,8 @@ def fa_backward_dropout(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float
                         p_drop: float, seed: int, offset: int = 0, stream=None):
     """fa_backward_dropout on [B, N, H, d] bf16 tensors (the forward's p_drop, seed, offset)."""
     B, N, H, d = _shape(q)
+    _same_shape("fa_backward_dropout", q, {"k": k, "v": v, "o": o, "do": do, "dq": dq, "dk": dk, "dv": dv})
+    _lse_shape("fa_backward_dropout", lse, B, H, N)
     _check((q, k, v, o, do, dq, dk, dv), torch.bfloat16)
     _check((lse, workspace), torch.float32)
     if workspace.numel() * 4 < fa_backward_workspace_bytes(B, H, N, d):

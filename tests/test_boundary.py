@@ -376,3 +376,73 @@ def test_python_binding_reports_status_names():
     from exact_io_aware_39_amd import fa_status_string, FaError
     assert fa_status_string(2).startswith("FA_ERR_UNSUPPORTED")
     assert "FA_ERR_INVALID_ARG" in str(FaError(1, "fa_forward"))
+
+
+def _bnhd(B=2, N=64, H=3, d=64, dtype=None):
+    import torch
+    return torch.zeros((B, N, H, d), dtype=dtype or torch.bfloat16)
+
+
+def _wrapper_calls():
+    """(name, call with every shape right, {tensor: wrong-shaped replacement})."""
+    import torch
+    import exact_io_aware_39_amd._lib as L
+    B, N, H, d = 2, 64, 3, 64
+    t = lambda: _bnhd(B, N, H, d)                                  # noqa: E731
+    lse = lambda: torch.zeros((B, H, N), dtype=torch.float32)       # noqa: E731
+    ws = lambda: torch.zeros(2 * B * H * N, dtype=torch.float32)    # noqa: E731
+    short, bad_lse = _bnhd(B, N - 8, H, d), torch.zeros((B, H, N - 8), dtype=torch.float32)
+    calls = [
+        ("fa_forward", lambda a: L.fa_forward(a["q"], a["k"], a["v"], a["o"], a["lse"], 0.1, True),
+         ["k", "v", "o", "lse"]),
+        ("fa_backward", lambda a: L.fa_backward(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                                               a["dk"], a["dv"], a["ws"], 0.1, True),
+         ["k", "v", "o", "do", "dq", "dk", "dv", "lse"]),
+        ("fa_backward_single_pass", lambda a: L.fa_backward_single_pass(
+            a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"], 0.1, True),
+         ["k", "v", "o", "do", "dq", "dk", "dv", "lse"]),
+        ("fa_backward_preprocess", lambda a: L.fa_backward_preprocess(a["o"], a["do"], a["lse"], a["ws"]),
+         ["do", "lse"]),
+        ("fa_backward_dqdkdv", lambda a: L.fa_backward_dqdkdv(a["q"], a["k"], a["v"], a["do"], a["ws"], a["dq"],
+                                                             a["dk"], a["dv"], 0.1, True),
+         ["k", "v", "do", "dq", "dk", "dv"]),
+        ("fa_backward_dkdv", lambda a: L.fa_backward_dkdv(a["q"], a["k"], a["v"], a["do"], a["ws"], a["dk"],
+                                                         a["dv"], 0.1, True),
+         ["k", "v", "do", "dk", "dv"]),
+        ("fa_backward_dq", lambda a: L.fa_backward_dq(a["q"], a["k"], a["v"], a["do"], a["ws"], a["dq"], 0.1, True),
+         ["k", "v", "do", "dq"]),
+        ("fa_forward_dropout", lambda a: L.fa_forward_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], 0.1, True,
+                                                             0.1, 1),
+         ["k", "v", "o", "lse"]),
+        ("fa_backward_dropout", lambda a: L.fa_backward_dropout(
+            a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"], 0.1, True, 0.1, 1),
+         ["k", "v", "o", "do", "dq", "dk", "dv", "lse"]),
+        ("fa_forward_cross", lambda a: L.fa_forward_cross(a["q"], a["k"], a["v"], a["o"], a["lse"], 0.1, False),
+         ["o", "lse"]),
+        ("fa_backward_cross", lambda a: L.fa_backward_cross(
+            a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"], 0.1, False),
+         ["o", "do", "dq", "dk", "dv", "lse"]),
+        ("fa_decode", lambda a: L.fa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], 0.1, False),
+         ["o", "lse"]),
+    ]
+    for name, call, wrong in calls:
+        def make(name=name):
+            return {"q": t(), "k": t(), "v": t(), "o": t(), "do": t(), "dq": t(), "dk": t(), "dv": t(),
+                    "lse": lse(), "ws": ws()}
+        yield name, call, make, wrong, short, bad_lse
+
+
+@pytest.mark.parametrize("case", list(_wrapper_calls()), ids=lambda c: c[0])
+def test_binding_rejects_mismatched_shapes(case):
+    """Each wrapper checks every tensor's shape against q's (lse against
+    [B, H, N]) before it touches the library, so a short K or a small LSE is
+    a ValueError, not an out-of-bounds device access.  The tensors here are on
+    the CPU: with the shapes right the call gets as far as the device check."""
+    name, call, make, wrong, short, bad_lse = case
+    with pytest.raises(ValueError, match="CUDA"):
+        call(make())
+    for which in wrong:
+        args = make()
+        args[which] = bad_lse if which == "lse" else short
+        with pytest.raises(ValueError, match="shape|must share"):
+            call(args)
