@@ -25,7 +25,7 @@ from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_cross, fa_backwar
                    fa_decode_splits, fa_decode_workspace_bytes, fa_forward, fa_forward_cross,
                    fa_forward_fp8, fa_forward_fp8_workspace_bytes, fa_status_string, load,
                    fa_forward_dropout, fa_backward_dropout, fa_backward_single_pass,
-                   fa_backward_single_pass_workspace_bytes)
+                   fa_backward_single_pass_workspace_bytes, fa_backward_noalloc)
 
 
 def _scale(q, scale):

@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH, FA_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -43,6 +43,8 @@ def load() -> ctypes.CDLL:
                        ("fa_backward", bwd_args), ("fa_backward_f32", bwd_args)):
         fn = getattr(lib, name)
         fn.argtypes, fn.restype = args, I
+    lib.fa_backward_noalloc.argtypes = [P] * 9 + [I, I, I, I, F, I, P]
+    lib.fa_backward_noalloc.restype = I
     lib.fa_backward_preprocess.argtypes = [P, P, P, P, I, I, I, I, P]
     lib.fa_backward_preprocess.restype = I
     for name, nptr in (("fa_backward_dqdkdv", 8), ("fa_backward_dkdv", 7), ("fa_backward_dq", 6)):
@@ -158,6 +160,19 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale: float, causal
     _call(name, fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                    _ptr(dv), _ptr(workspace), B, H, N, d, float(scale), int(bool(causal)),
                    _stream(stream)))
+
+
+def fa_backward_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, stream=None):
+    """fa_backward_noalloc on [B, N, H, d] bf16 tensors: fa_backward with the
+    library's static scratch in place of a workspace (B*H*N <= 2^21)."""
+    B, N, H, d = _shape(q)
+    _same_shape("fa_backward_noalloc", q, {"k": k, "v": v, "o": o, "do": do, "dq": dq, "dk": dk, "dv": dv})
+    _lse_shape("fa_backward_noalloc", lse, B, H, N)
+    _check((q, k, v, o, do, dq, dk, dv), torch.bfloat16)
+    _check((lse,), torch.float32)
+    _call("fa_backward_noalloc", load().fa_backward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, H, N, d, float(scale), int(bool(causal)), _stream(stream)))
 
 
 def fa_backward_single_pass_workspace_bytes(B: int, H: int, N: int, d: int) -> int:

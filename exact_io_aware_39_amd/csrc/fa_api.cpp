@@ -274,17 +274,30 @@ size_t fa_backward_single_pass_workspace_bytes(int B, int H, int N, int d) {
   return ((size_t)fa::bwd_single_pass_acc_offset(B, H, N) + (size_t)B * N * H * d) * sizeof(float);
 }
 
+fa_status fa_backward_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                              const float* LSE, void* dQ, void* dK, void* dV,
+                              int B, int H, int N, int d, float scale, int causal, void* stream) {
+  fa_status st = check_common(B, H, N, d, scale, causal, true);
+  if (st == FA_OK) st = check_tensors({Q, K, V, O, dO, dQ, dK, dV}, {LSE});
+  if (st == FA_OK && (int64_t)B * H * N > fa::kNoallocMaxRows) st = FA_ERR_SCRATCH_LIMIT;
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal};
+  return to_status(fa::launch_bwd_bf16_noalloc(Q, K, V, O, dO, LSE, dQ, dK, dV, s,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   if (check_common(B, H, N, d, 1.f, 0, true) != FA_OK) return 0;
   return 2 * (size_t)B * H * N * sizeof(float);
 }
 
-const char* fa_status_string(int status) {
+const char* fa_status_string(fa_status status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument (null or misaligned pointer, bad size, scale or mask flag)";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration (head size without kernels for this entry point, negative scale, or size limits)";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: a HIP launch failed";
+    case FA_ERR_SCRATCH_LIMIT: return "FA_ERR_SCRATCH_LIMIT: fa_backward_noalloc needs B*H*N <= 2^21 query rows (its static scratch holds 16 MiB); use fa_backward with a workspace";
     default: return "unknown fa_status";
   }
 }

@@ -82,6 +82,13 @@ int decode_splits(int B, int H, int Nq, int Nk);
 hipError_t launch_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                               float* ws, const DecodeShape& s, hipStream_t stream);
 
+// fa_backward with its workspace in the library's static scratch array
+// (fa_noalloc.hip); B H N <= kNoallocMaxRows, checked by the caller.
+constexpr int64_t kNoallocMaxRows = int64_t(1) << 21;
+hipError_t launch_bwd_bf16_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                   const AttnShape& s, hipStream_t stream);
+
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                           const float* dout, const float* lse, float* dq, float* dk, float* dv,
                           float* dvec, const AttnShape& s, hipStream_t stream);

@@ -68,7 +68,8 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1,
   FA_ERR_UNSUPPORTED = 2,
-  FA_ERR_LAUNCH = 3
+  FA_ERR_LAUNCH = 3,
+  FA_ERR_SCRATCH_LIMIT = 4   /* fa_backward_noalloc only: B*H*N above its scratch */
 } fa_status;
 
 /*
@@ -286,8 +287,26 @@ int fa_decode_splits(int B, int H, int Nq, int Nk, int d);
    chunks (splits, or fa_decode_splits() for splits = 0); 0 for invalid sizes. */
 size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int splits);
 
+/*
+ * fa_backward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments (minus `workspace`), results (bitwise
+ * those of fa_backward) and checks as fa_backward; its 8 B H N bytes of
+ * scratch are a static array of the library, 16 MiB on each GPU it runs on,
+ * held from the library's first use of that GPU until the process ends.  The
+ * call allocates and frees nothing.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (different streams, or threads without
+ * ordering) race and give undefined results.  Nothing in the array needs to be
+ * cleared between calls (each call overwrites what it reads).
+ * Errors as fa_backward, and FA_ERR_SCRATCH_LIMIT when B*H*N > 2^21 (the
+ * array holds two fp32 words per query row); on error nothing is enqueued.
+ */
+fa_status fa_backward_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                              const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                              int B, int H, int N, int d, float scale, int causal, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
-const char* fa_status_string(int status);
+const char* fa_status_string(fa_status status);
 
 #ifdef __cplusplus
 }

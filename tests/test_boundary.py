@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 LIB = os.path.join(ROOT, "exact_io_aware_39_amd", "libfa.so")
 
-OK, INVALID, UNSUPPORTED, LAUNCH = 0, 1, 2, 3
+OK, INVALID, UNSUPPORTED, LAUNCH, SCRATCH_LIMIT = 0, 1, 2, 3, 4
 P = 0x10000          # a 16-byte aligned fake device address
 
 
@@ -58,6 +58,8 @@ def lib():
     lib.fa_decode_splits.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i] * 6
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_backward_noalloc.argtypes = [vp] * 9 + [i] * 4 + [f, i, vp]
+    lib.fa_backward_noalloc.restype = i
     lib.fa_backward_single_pass.argtypes = [vp] * 10 + [i] * 4 + [f, i, vp]
     lib.fa_backward_single_pass.restype = i
     lib.fa_backward_single_pass_workspace_bytes.argtypes = [i] * 4
@@ -82,7 +84,8 @@ def test_header_declares_the_expected_entry_points():
         "fa_decode", "fa_decode_splits", "fa_decode_workspace_bytes", "fa_forward_cross",
         "fa_backward_cross", "fa_forward_fp8", "fa_forward_fp8_workspace_bytes",
         "fa_forward_dropout", "fa_backward_dropout",
-        "fa_backward_single_pass", "fa_backward_single_pass_workspace_bytes"])
+        "fa_backward_single_pass", "fa_backward_single_pass_workspace_bytes",
+        "fa_backward_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -169,6 +172,26 @@ def test_single_pass_rejects_bad_arguments(lib):
     ptrs = [P] * 10
     ptrs[5] = P + 2                             # LSE: 4-byte alignment
     assert _bwd(lib, name, ptrs=tuple(ptrs)) == INVALID
+
+
+def test_noalloc_rejects_bad_arguments(lib):
+    """The allocation-free backward: fa_backward's checks, and the size of its
+    static scratch (2^21 query rows), all before any HIP call."""
+    def call(ptrs=(P,) * 9, B=1, H=1, N=128, d=64, scale=0.125, causal=0):
+        return lib.fa_backward_noalloc(*ptrs, B, H, N, d, scale, causal, None)
+    assert call(d=80) == UNSUPPORTED
+    assert call(N=0) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(causal=2) == INVALID
+    for i in range(9):
+        ptrs = [P] * 9
+        ptrs[i] = None
+        assert call(ptrs=tuple(ptrs)) == INVALID
+    assert call(ptrs=(P,) * 5 + (P + 2,) + (P,) * 3) == INVALID       # LSE 4-byte alignment
+    assert call(ptrs=(P + 4,) + (P,) * 8) == INVALID                  # Q 16-byte alignment
+    assert call(B=1, H=32, N=65537) == SCRATCH_LIMIT
+    assert call(B=4, H=16, N=32769) == SCRATCH_LIMIT
+    assert call(B=2, H=16, N=65537, d=256) == SCRATCH_LIMIT
 
 
 def test_single_pass_workspace_bytes(lib):
@@ -367,7 +390,8 @@ def test_decode_splits_and_workspace(lib):
 
 def test_status_strings(lib):
     for code, key in ((OK, b"FA_OK"), (INVALID, b"FA_ERR_INVALID_ARG"),
-                      (UNSUPPORTED, b"FA_ERR_UNSUPPORTED"), (LAUNCH, b"FA_ERR_LAUNCH")):
+                      (UNSUPPORTED, b"FA_ERR_UNSUPPORTED"), (LAUNCH, b"FA_ERR_LAUNCH"),
+                      (SCRATCH_LIMIT, b"FA_ERR_SCRATCH_LIMIT")):
         assert lib.fa_status_string(code).startswith(key)
     assert b"unknown" in lib.fa_status_string(99)
 
