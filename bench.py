@@ -19,6 +19,17 @@ workloads ([4, 4096, 16, 128] and [1, 32768, 32, 128] with Q, K doubled).
     python bench.py --copy-calibration
 
 runs only a plain device copy of 256 MiB (for scaling hardware byte counters).
+
+    python bench.py --kernel-case {c5,c3_causal,c3_noncausal,c4,c2} [--steps K]
+
+runs only that workload's launches (c5: the forward + backward step; the
+others: the forward), for profiling one kernel under rocprofv3.
+
+Besides the back-to-back timing that gives `value`, the line carries per-kernel
+median, p10 and p90 of the same launches, a cold-cache timing of the step (a
+512 MiB buffer, twice the 256 MB Infinity Cache, is written before each step),
+the shader clock measured while the step runs, and the host's core counts
+beside the CPU baseline.
 """
 from __future__ import annotations
 
@@ -86,6 +97,55 @@ def warm_up(fn, torch, min_seconds=0.2):
             return
 
 
+def pct(xs, q):
+    """q-quantile of a list (nearest rank)."""
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
+def stats_ms(xs):
+    return {"median": round(pct(xs, 0.5), 4), "p10": round(pct(xs, 0.1), 4), "p90": round(pct(xs, 0.9), 4),
+            "mean": round(sum(xs) / len(xs), 4)}
+
+
+def sclk_under_load(step, torch, cycles=20_000_000, load_steps=25):
+    """Shader clock (MHz) while `step` runs.  A one-wave spin of a fixed
+    number of shader-clock cycles (torch.cuda._sleep, which counts the
+    shader clock) runs on a second stream of default priority while the main
+    stream runs `load_steps` steps before and after it; cycles / elapsed time
+    of the spin, between events on its own stream, is the clock under that
+    load.  The same spin on an idle GPU gives the clock at low load."""
+    side = torch.cuda.Stream()
+    out = {}
+    for name, load in (("idle", 0), ("under_load", load_steps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(load):
+            step()
+        with torch.cuda.stream(side):
+            e0.record(side)
+            torch.cuda._sleep(cycles)
+            e1.record(side)
+        for _ in range(load):
+            step()
+        torch.cuda.synchronize()
+        out[name] = round(cycles / (e0.elapsed_time(e1) * 1e-3) / 1e6, 1)
+    out["source"] = ("a spin of %d shader-clock cycles (torch.cuda._sleep) on a side stream, timed with "
+                     "events, alone and beside %d fwd+bwd steps on each side" % (cycles, load_steps))
+    return out
+
+
+def host_cores():
+    """os.cpu_count(), the affinity mask's size and the BLAS thread count."""
+    blas = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"), default=None)
+    except Exception:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "blas_threads": blas}
+
+
 def time_forward_only(fa, torch, B, N, H, d, scale, qk_mult, seed, iters, causal=True):
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
@@ -107,6 +167,7 @@ def time_forward_only(fa, torch, B, N, H, d, scale, qk_mult, seed, iters, causal
     tf = fwd_flops(B, H, N, d, causal) / (med * 1e-3) / 1e12
     del q, k, v, o, lse
     return {"shape_BNHd": [B, N, H, d], "causal": causal, "median_ms": round(med, 4),
+            "p10_ms": round(pct(ms, 0.1), 4), "p90_ms": round(pct(ms, 0.9), 4),
             "tflops": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
 
 
@@ -283,8 +344,23 @@ def cpu_baseline(w, host, got, min_seconds=10.0):
         "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
         "sample": (f"fp64 numpy oracle, forward + backward of {done} whole head(s) of the same workload "
                    f"(N={w.N}, d={w.d}, causal) in {dt:.1f} s; credited FLOPs as for the GPU"),
-        "seconds": round(dt, 2),
+        "seconds": round(dt, 2), "host": host_cores(),
     }, errs
+
+
+def kernel_case(fa, torch, synth, name, steps):
+    """Launches of one workload only (for profiling one kernel): `steps`
+    launches after a time-based warm-up; prints a short line."""
+    cases = {
+        "c3_causal": (4, 4096, 16, 128, True, 1.0, 3),
+        "c3_noncausal": (4, 4096, 16, 128, False, 1.0, 3),
+        "c4": (1, 32768, 32, 128, True, 2.0, 4),
+        "c2": (2, 512, 8, 64, True, 1.0, 2),
+    }
+    B, N, H, d, causal, mult, seed = cases[name]
+    r = time_forward_only(fa, torch, B, N, H, d, synth.f32(d ** -0.5) if d != 64 else 0.125, mult, seed, steps,
+                          causal=causal)
+    print(json.dumps({"kernel_case": name, **r}), flush=True)
 
 
 def main():
@@ -295,6 +371,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--kernel-case", choices=["c5", "c3_causal", "c3_noncausal", "c4", "c2"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (heads would shard "
@@ -313,6 +390,9 @@ def main():
     fa.load()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.kernel_case and args.kernel_case != "c5":
+        kernel_case(fa, torch, synth, args.kernel_case, args.steps)
         return
 
     w = synth.WORKLOADS["c5"]
@@ -340,8 +420,20 @@ def main():
         if evs:
             evs[3].record(st)
 
+    if args.kernel_case == "c5":
+        warm_up(step, torch)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_case": "c5", "steps": args.steps}), flush=True)
+        return
+
+    names = ["fwd", "bwd_preprocess", "bwd_dqdkdv"]
+    # Warm-up: the requested count, and at least 0.2 s of load so that the
+    # shader clock has come up before the timed steps.
     for _ in range(args.warmup):
         step()
+    warm_up(step, torch)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -349,8 +441,21 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ["fwd", "bwd_preprocess", "bwd_dqdkdv"]
-    per = {n: [events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)] for j, n in enumerate(names)}
+    per = {n: [events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]
+           for j, n in enumerate(names)}
+    # Cold caches: before each step, write 512 MiB (twice the Infinity
+    # Cache) so that no input of the step is left in L2 or MALL.
+    ncold = min(args.steps, 20)
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ncold)]
+    for i in range(ncold):
+        flush.fill_(float(i))
+        step(cold_ev[i])
+    torch.cuda.synchronize()
+    cold = {n: [cold_ev[i][j].elapsed_time(cold_ev[i][j + 1]) for i in range(ncold)]
+            for j, n in enumerate(names)}
+    cold_step = [cold_ev[i][0].elapsed_time(cold_ev[i][3]) for i in range(ncold)]
+    del flush
     avg = {n: sum(x) / len(x) for n, x in per.items()}
     ms_step = wall * 1e3 / args.steps
 
@@ -384,6 +489,10 @@ def main():
     if dom in executed:
         roof["executed_mfma_tflops"] = round(executed[dom] / (avg[dom] * 1e-3) / 1e12, 1)
     roof["traffic"] = kernel_traffic(dom)
+    sclk = sclk_under_load(step, torch)
+    if bound == "mfma" and sclk.get("under_load"):
+        # the same launch against the MFMA rate at the clock observed under this load
+        roof["frac_at_observed_sclk"] = round(achieved / (PEAK_BF16_TFLOPS * sclk["under_load"] / 2400.0), 4)
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1,
@@ -401,17 +510,31 @@ def main():
             "fwd_pct_of_peak": round(100 * F / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
             "bwd_pct_of_peak_credited": round(100 * Fb / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
             "kernel_avg_ms": {n: round(x, 4) for n, x in avg.items()},
+            "kernel_ms": {n: stats_ms(x) for n, x in per.items()},
         },
+        "cold_cache": {
+            "note": "512 MiB written before each step (caches cold); per-kernel times in ms",
+            "steps": ncold, "step_ms": stats_ms(cold_step),
+            "kernel_ms": {n: stats_ms(x) for n, x in cold.items()},
+            "fwd_pct_of_peak": round(100 * F / (pct(cold["fwd"], 0.5) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "bwd_pct_of_peak_credited": round(100 * Fb / ((pct(cold["bwd_preprocess"], 0.5)
+                                                           + pct(cold["bwd_dqdkdv"], 0.5)) * 1e-3)
+                                              / 1e12 / PEAK_BF16_TFLOPS, 2),
+        },
+        "sclk": sclk,
+        "host": host_cores(),
     }
 
     if not args.no_extra:
-        log("bench: forward-only long causal workloads")
+        log("bench: forward-only workloads")
         result["forward_only"] = {
+            "c2": time_forward_only(fa, torch, 2, 512, 8, 64, 0.125, 1.0, 2, 50),
             "c3_causal": time_forward_only(fa, torch, 4, 4096, 16, 128, synth.f32(128 ** -0.5), 1.0, 3, 20),
             "c3_noncausal": time_forward_only(fa, torch, 4, 4096, 16, 128, synth.f32(128 ** -0.5), 1.0, 3, 20,
                                               causal=False),
             "c4": time_forward_only(fa, torch, 1, 32768, 32, 128, synth.f32(128 ** -0.5), 2.0, 4, 10),
         }
+        result["forward_only"]["c2"]["note"] = "reported, not targeted (64 workgroups for 256 CUs)"
         log("bench: FP8 (e4m3) forward")
         result["forward_fp8"] = {
             "c3_causal": time_forward_fp8(fa, torch, 4, 4096, 16, 128, 3, 20),
