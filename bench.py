@@ -69,9 +69,17 @@ def copy_calibration():
     log(f"copy calibration: 3 launches, each reads {n * 4} B and writes {n * 4} B")
 
 
+# counter summary of each kernel of the c5 step (profiles/)
+COUNTER_FILES = {"fwd": "counters_fwd_d64_causal.md", "bwd_dqdkdv": "counters_bwd_dqdkdv.md",
+                 "bwd_preprocess": "counters_bwd_preprocess.md"}
+
+
 def kernel_traffic(name):
-    """HBM bytes per launch from a committed counter summary, if it matches the source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.md")
+    """HBM bytes per launch (TCC read and write request counts, copy-calibrated)
+    from the committed counter summary, if it matches the current source."""
+    if name not in COUNTER_FILES:
+        return None
+    path = os.path.join(ROOT, "profiles", COUNTER_FILES[name])
     if not os.path.exists(path):
         return None
     text = open(path).read()
