@@ -1,20 +1,36 @@
-// fa_f32.hip - float32 forward and backward (correctness path, plain VALU).
+// fa_f32.hip - float32 forward and backward on the fp32 matrix cores.
 //
-// Same algorithm as the bf16 kernels, in fp32 throughout and without matrix
-// cores: tiles of K and V pass through LDS, each thread owns one query row (or
-// one key row in the dK/dV pass) and keeps its running max, running sum and
-// unnormalised output in registers (page "FlashAttention", vagrantpi.github.io
-// PKM note, "三招" items 1-3).  The backward rebuilds P = exp(scale q k^T - LSE)
-// and follows the chain rule of softmax: dV = P^T dO, dP = dO V^T,
-// D = rowsum(dO * O), dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+// Same algorithm as the bf16 kernels, in fp32 throughout: tiles of the
+// streamed operand pass through LDS, the running max, running sum and the
+// unnormalised output stay in registers (page "FlashAttention", vagrantpi
+// PKM note, "三招" items 1-3: tiling, online softmax, recomputation).  The
+// backward rebuilds P = exp(scale q k^T - LSE) and follows the chain rule of
+// softmax: dV = P^T dO, dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D),
+// dQ = scale dS K, dK = scale dS^T Q.
+//
+// Every product runs on v_mfma_f32_16x16x4_f32 (wave64, one block):
+//   A (16 x 4): lane l holds row l%16, k = l/16
+//   B (4 x 16): lane l holds column l%16, k = l/16
+//   C (16 x 16): lane l, register r holds row 4*(l/16) + r, column l%16
+// A contraction may visit k in any order as long as A and B agree, so the
+// kernels pick the order that lets each lane read four consecutive floats,
+// and they feed a C fragment straight back in as the B operand of the next
+// product: with S^T = K Q^T in C layout, lane l already holds P^T for keys
+// 4*(l/16) + r of its query column, which is what O^T = V^T P^T needs as B
+// when step r of the contraction maps lane group l/16 to key 4*(l/16) + r.
+// The A operand of that product (V^T, Q^T, dO^T or K^T) is kept transposed in
+// LDS so that the same four keys are one 16-byte read.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
 namespace {
 
-constexpr int kRows = 64;   // query (or key) rows per workgroup, one per thread
-constexpr int kTile = 32;   // rows of the streamed operand per step
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 16 * kWaves;   // resident rows per workgroup, 16 per wave
+constexpr int kTile = 32;            // streamed rows per LDS stage
+constexpr int kPad = 4;              // floats of padding per LDS row
 
 struct F32Args {
   const float* q;
@@ -30,6 +46,23 @@ struct F32Args {
   float scale;
 };
 
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
+
+// Reductions over the four lanes l, l^16, l^32, l^48 that share a column.
+__device__ __forceinline__ float col_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float col_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
 template <int D>
 __device__ __forceinline__ void bh_coords(const F32Args& a, int& bh, int& tile, int64_t& base) {
   bh = blockIdx.x / a.ntiles;
@@ -38,65 +71,142 @@ __device__ __forceinline__ void bh_coords(const F32Args& a, int& bh, int& tile, 
   base = ((int64_t)b * a.N * a.H + h) * D;
 }
 
+// Stage kTile rows of `src` starting at row r0 into LDS: row-major (stride
+// D + kPad) into `rm` and, if `tr` is given, transposed (stride kTile + kPad)
+// into `tr`.  Rows past N read as zero.
+template <int D>
+__device__ __forceinline__ void stage(const float* src, int64_t base, int64_t rs, int r0, int N,
+                                      float* rm, float* tr) {
+  constexpr int C4 = D / 4;
+  for (int idx = threadIdx.x; idx < kTile * C4; idx += kThreads) {
+    const int r = idx / C4, c = (idx - r * C4) * 4;
+    const int row = r0 + r;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < N) x = ld4(src + base + (int64_t)row * rs + c);
+    if (rm) st4(rm + r * (D + kPad) + c, x);
+    if (tr) {
+      tr[(c + 0) * (kTile + kPad) + r] = x.x;
+      tr[(c + 1) * (kTile + kPad) + r] = x.y;
+      tr[(c + 2) * (kTile + kPad) + r] = x.z;
+      tr[(c + 3) * (kTile + kPad) + r] = x.w;
+    }
+  }
+}
+
+// C += X Y^T over the head dimension for one 16 x 16 tile, where lane l
+// supplies row l%16 of X from LDS (row-major, stride D + kPad, starting at
+// row x0) and its own 16 B-operand floats of Y (row l%16 of Y at columns
+// 16c + 4(l/16) .. +3, c = 0 .. D/16 - 1).
+template <int D>
+__device__ __forceinline__ f32x4 dot_rows(const float* xs, int x0, const float4 (&y)[D / 16], f32x4 c) {
+  const int lane = threadIdx.x & 63;
+  const float* xr = xs + (x0 + (lane & 15)) * (D + kPad) + 4 * (lane >> 4);
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) {
+    const float4 x = ld4(xr + 16 * cc);
+    c = mma(x.x, y[cc].x, c);
+    c = mma(x.y, y[cc].y, c);
+    c = mma(x.z, y[cc].z, c);
+    c = mma(x.w, y[cc].w, c);
+  }
+  return c;
+}
+
+// acc[dt] += Xt[16dt .. 16dt+15, t0 + 0 .. 15] * F, where Xt is a transposed
+// LDS tile (stride kTile + kPad) and F is a C fragment (rows t0 + 4(l/16) + r
+// of the contraction, column l%16) used as the B operand.
+template <int D>
+__device__ __forceinline__ void acc_tr(f32x4 (&acc)[D / 16], const float* xt, int t0, const f32x4& f) {
+  const int lane = threadIdx.x & 63;
+  const float* xr = xt + (lane & 15) * (kTile + kPad) + t0 + 4 * (lane >> 4);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const float4 x = ld4(xr + 16 * dt * (kTile + kPad));
+    acc[dt] = mma(x.x, f[0], acc[dt]);
+    acc[dt] = mma(x.y, f[1], acc[dt]);
+    acc[dt] = mma(x.z, f[2], acc[dt]);
+    acc[dt] = mma(x.w, f[3], acc[dt]);
+  }
+}
+
+// Lane l's 16 B-operand floats of one row: row[16c + 4(l/16) .. +3].
+template <int D>
+__device__ __forceinline__ void load_row(float4 (&y)[D / 16], const float* row) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) y[cc] = ld4(row + 16 * cc + 4 * g);
+}
+
+// Store a transposed accumulator (rows = head dimension, column l%16 = the
+// lane's row of the output) as the lane's slice of that output row.
+template <int D>
+__device__ __forceinline__ void store_row(float* row, const f32x4 (&acc)[D / 16], float mul) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    st4(row + 16 * dt + 4 * g, make_float4(acc[dt][0] * mul, acc[dt][1] * mul, acc[dt][2] * mul, acc[dt][3] * mul));
+}
+
+// Forward: wave w owns queries tile*64 + 16w + l%16 (the columns of S^T).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kRows) void fwd_f32_kernel(F32Args a) {
-  __shared__ float ks[kTile][D];
-  __shared__ float vs[kTile][D];
+__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
+  __shared__ float ks[kTile * (D + kPad)];
+  __shared__ float vt[D * (kTile + kPad)];
   int bh, tile;
   int64_t base;
   bh_coords<D>(a, bh, tile, base);
-  const int N = a.N, tid = threadIdx.x;
+  const int N = a.N, lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int64_t rs = (int64_t)a.H * D;
-  const int myq = tile * kRows + tid;
+  const int qw = tile * kRows + 16 * w;   // first query of this wave
+  const int myq = qw + (lane & 15);
 
-  float q[D], o[D];
-  const float* qrow = a.q + base + (int64_t)min(myq, N - 1) * rs;
+  float4 qv[D / 16];
+  load_row<D>(qv, a.q + base + (int64_t)min(myq, N - 1) * rs);
+  f32x4 o[D / 16];
 #pragma unroll
-  for (int c = 0; c < D; ++c) { q[c] = qrow[c]; o[c] = 0.f; }
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
   const int kend = CAUSAL ? min(N, tile * kRows + kRows) : N;
   for (int k0 = 0; k0 < kend; k0 += kTile) {
     __syncthreads();
-    for (int idx = tid; idx < kTile * D; idx += kRows) {
-      const int r = idx / D, c = idx % D;
-      const int key = k0 + r;
-      ks[r][c] = key < N ? a.k[base + (int64_t)key * rs + c] : 0.f;
-      vs[r][c] = key < N ? a.v[base + (int64_t)key * rs + c] : 0.f;
-    }
+    stage<D>(a.k, base, rs, k0, N, ks, nullptr);
+    stage<D>(a.v, base, rs, k0, N, nullptr, vt);
     __syncthreads();
-    float s[kTile];
+    if (CAUSAL && k0 > qw + 15) continue;   // the whole stage is above this wave's diagonal
+    f32x4 s[kTile / 16];
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      float dot = 0.f;
+    for (int t = 0; t < kTile / 16; ++t) {
+      s[t] = dot_rows<D>(ks, 16 * t, qv, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int c = 0; c < D; ++c) dot = __builtin_fmaf(q[c], ks[j][c], dot);
-      const int key = k0 + j;
-      s[j] = (key >= N || (CAUSAL && key > myq)) ? -INFINITY : dot * a.scale;
-      mx = fmaxf(mx, s[j]);
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + 16 * t + 4 * g + r;
+        s[t][r] = (key >= N || (CAUSAL && key > myq)) ? -INFINITY : s[t][r] * a.scale;
+        mx = fmaxf(mx, s[t][r]);
+      }
     }
+    mx = col_max(mx);
     const float m_new = fmaxf(m, mx);
-    if (m_new == -INFINITY) continue;        // nothing visible yet for this row
     const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
-    l *= alpha;
+    float ps = 0.f;
 #pragma unroll
-    for (int c = 0; c < D; ++c) o[c] *= alpha;
+    for (int t = 0; t < kTile / 16; ++t)
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      const float p = (s[j] == -INFINITY) ? 0.f : expf(s[j] - m_new);
-      l += p;
-#pragma unroll
-      for (int c = 0; c < D; ++c) o[c] = __builtin_fmaf(p, vs[j][c], o[c]);
-    }
+      for (int r = 0; r < 4; ++r) {
+        s[t][r] = (s[t][r] == -INFINITY) ? 0.f : expf(s[t][r] - m_new);
+        ps += s[t][r];
+      }
+    l = l * alpha + col_sum(ps);
     m = m_new;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+#pragma unroll
+    for (int t = 0; t < kTile / 16; ++t) acc_tr<D>(o, vt, 16 * t, s[t]);
   }
   if (myq < N) {
-    float* orow = a.out0 + base + (int64_t)myq * rs;
-    const float inv = 1.f / l;
-#pragma unroll
-    for (int c = 0; c < D; ++c) orow[c] = o[c] * inv;
-    a.out1[(int64_t)bh * N + myq] = m + logf(l);
+    store_row<D>(a.out0 + base + (int64_t)myq * rs, o, 1.f / l);
+    if (g == 0) a.out1[(int64_t)bh * N + myq] = m + logf(l);
   }
 }
 
@@ -116,132 +226,119 @@ __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(const float* o, const 
   dvec[(b * H + h) * N + n] = acc;
 }
 
-// dK, dV for 64 keys (one per thread), walking every query that can see them.
+// dK, dV: wave w owns keys tile*64 + 16w + l%16 (the columns of S = Q K^T)
+// and walks every query that can see them, 32 per LDS stage.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(F32Args a) {
-  __shared__ float qs[kTile][D];
-  __shared__ float gs[kTile][D];
-  __shared__ float kv[2][kRows][D + 1];
-  __shared__ float ls[kTile], ds[kTile];
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(F32Args a) {
+  __shared__ float qs[kTile * (D + kPad)];
+  __shared__ float gs[kTile * (D + kPad)];
+  __shared__ float qt[D * (kTile + kPad)];
+  __shared__ float gt[D * (kTile + kPad)];
+  __shared__ float ls[kTile], dd[kTile];
   int bh, tile;
   int64_t base;
   bh_coords<D>(a, bh, tile, base);
-  const int N = a.N, tid = threadIdx.x;
+  const int N = a.N, lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int64_t rs = (int64_t)a.H * D;
-  const int k0 = tile * kRows;
-  const int myk = k0 + tid;
-  for (int idx = tid; idx < kRows * D; idx += kRows) {
-    const int r = idx / D, c = idx % D;
-    const int key = min(k0 + r, N - 1);
-    kv[0][r][c] = a.k[base + (int64_t)key * rs + c];
-    kv[1][r][c] = a.v[base + (int64_t)key * rs + c];
-  }
-  float dk[D], dv[D];
+  const int kw = tile * kRows + 16 * w;   // first key of this wave
+  const int myk = kw + (lane & 15);
+
+  float4 kv[D / 16], vv[D / 16];
+  load_row<D>(kv, a.k + base + (int64_t)min(myk, N - 1) * rs);
+  load_row<D>(vv, a.v + base + (int64_t)min(myk, N - 1) * rs);
+  f32x4 dk[D / 16], dv[D / 16];
 #pragma unroll
-  for (int c = 0; c < D; ++c) { dk[c] = 0.f; dv[c] = 0.f; }
+  for (int dt = 0; dt < D / 16; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float* lse = a.lse + (int64_t)bh * N;
   const float* dvec = a.dvec + (int64_t)bh * N;
-  const int qstart = CAUSAL ? (k0 / kTile) * kTile : 0;
+
+  const int qstart = CAUSAL ? tile * kRows : 0;   // earlier queries see none of these keys
   for (int i0 = qstart; i0 < N; i0 += kTile) {
     __syncthreads();
-    for (int idx = tid; idx < kTile * D; idx += kRows) {
-      const int r = idx / D, c = idx % D;
-      const int qi = min(i0 + r, N - 1);
-      qs[r][c] = a.q[base + (int64_t)qi * rs + c];
-      gs[r][c] = a.dout[base + (int64_t)qi * rs + c];
-    }
-    if (tid < kTile) {
-      const int qi = min(i0 + tid, N - 1);
-      ls[tid] = lse[qi];
-      ds[tid] = dvec[qi];
+    stage<D>(a.q, base, rs, i0, N, qs, qt);
+    stage<D>(a.dout, base, rs, i0, N, gs, gt);
+    if (threadIdx.x < kTile) {
+      const int qi = i0 + threadIdx.x;
+      ls[threadIdx.x] = qi < N ? lse[qi] : 0.f;
+      dd[threadIdx.x] = qi < N ? dvec[qi] : 0.f;
     }
     __syncthreads();
-    for (int r = 0; r < kTile; ++r) {
-      const int qi = i0 + r;
-      if (qi >= N || (CAUSAL && myk > qi)) continue;
-      float s = 0.f, dp = 0.f;
+    if (CAUSAL && i0 + kTile - 1 < kw) continue;   // no query of the stage sees this wave's keys
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        s = __builtin_fmaf(qs[r][c], kv[0][tid][c], s);
-        dp = __builtin_fmaf(gs[r][c], kv[1][tid][c], dp);
-      }
-      const float p = expf(s * a.scale - ls[r]);
-      const float dsv = p * (dp - ds[r]);
+    for (int u = 0; u < kTile / 16; ++u) {
+      f32x4 s = dot_rows<D>(qs, 16 * u, kv, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 dp = dot_rows<D>(gs, 16 * u, vv, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        dv[c] = __builtin_fmaf(p, gs[r][c], dv[c]);
-        dk[c] = __builtin_fmaf(dsv, qs[r][c], dk[c]);
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * u + 4 * g + r;
+        const int qi = i0 + row;
+        const bool vis = qi < N && !(CAUSAL && myk > qi);
+        const float p = vis ? expf(s[r] * a.scale - ls[row]) : 0.f;
+        s[r] = p;
+        dp[r] = p * (dp[r] - dd[row]);
       }
+      acc_tr<D>(dv, gt, 16 * u, s);
+      acc_tr<D>(dk, qt, 16 * u, dp);
     }
   }
   if (myk < N) {
-    float* dkrow = a.out0 + base + (int64_t)myk * rs;
-    float* dvrow = a.out1 + base + (int64_t)myk * rs;
-#pragma unroll
-    for (int c = 0; c < D; ++c) { dkrow[c] = dk[c] * a.scale; dvrow[c] = dv[c]; }
+    store_row<D>(a.out0 + base + (int64_t)myk * rs, dk, a.scale);
+    store_row<D>(a.out1 + base + (int64_t)myk * rs, dv, 1.f);
   }
 }
 
-// dQ for 64 queries (one per thread), walking every key they can see.
+// dQ: wave w owns queries tile*64 + 16w + l%16 (the columns of S^T = K Q^T)
+// and walks every key they can see, 32 per LDS stage.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(F32Args a) {
-  __shared__ float ks[kTile][D];
-  __shared__ float vs[kTile][D];
-  __shared__ float qg[2][kRows][D + 1];
+__global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(F32Args a) {
+  __shared__ float ks[kTile * (D + kPad)];
+  __shared__ float vs[kTile * (D + kPad)];
+  __shared__ float kt[D * (kTile + kPad)];
   int bh, tile;
   int64_t base;
   bh_coords<D>(a, bh, tile, base);
-  const int N = a.N, tid = threadIdx.x;
+  const int N = a.N, lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
   const int64_t rs = (int64_t)a.H * D;
-  const int q0 = tile * kRows;
-  const int myq = q0 + tid;
-  for (int idx = tid; idx < kRows * D; idx += kRows) {
-    const int r = idx / D, c = idx % D;
-    const int qi = min(q0 + r, N - 1);
-    qg[0][r][c] = a.q[base + (int64_t)qi * rs + c];
-    qg[1][r][c] = a.dout[base + (int64_t)qi * rs + c];
-  }
+  const int qw = tile * kRows + 16 * w;
+  const int myq = qw + (lane & 15);
   const int qc = min(myq, N - 1);
+
+  float4 qv[D / 16], gv[D / 16];
+  load_row<D>(qv, a.q + base + (int64_t)qc * rs);
+  load_row<D>(gv, a.dout + base + (int64_t)qc * rs);
   const float lse = a.lse[(int64_t)bh * N + qc];
   const float dvl = a.dvec[(int64_t)bh * N + qc];
-  float dq[D];
+  f32x4 dq[D / 16];
 #pragma unroll
-  for (int c = 0; c < D; ++c) dq[c] = 0.f;
-  const int kend = CAUSAL ? min(N, q0 + kRows) : N;
+  for (int dt = 0; dt < D / 16; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kend = CAUSAL ? min(N, tile * kRows + kRows) : N;
   for (int k0 = 0; k0 < kend; k0 += kTile) {
     __syncthreads();
-    for (int idx = tid; idx < kTile * D; idx += kRows) {
-      const int r = idx / D, c = idx % D;
-      const int key = min(k0 + r, N - 1);
-      ks[r][c] = a.k[base + (int64_t)key * rs + c];
-      vs[r][c] = a.v[base + (int64_t)key * rs + c];
-    }
+    stage<D>(a.k, base, rs, k0, N, ks, kt);
+    stage<D>(a.v, base, rs, k0, N, vs, nullptr);
     __syncthreads();
-    for (int j = 0; j < kTile; ++j) {
-      const int key = k0 + j;
-      if (key >= N || (CAUSAL && key > myq)) continue;
-      float s = 0.f, dp = 0.f;
+    if (CAUSAL && k0 > qw + 15) continue;
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        s = __builtin_fmaf(qg[0][tid][c], ks[j][c], s);
-        dp = __builtin_fmaf(qg[1][tid][c], vs[j][c], dp);
+    for (int t = 0; t < kTile / 16; ++t) {
+      f32x4 s = dot_rows<D>(ks, 16 * t, qv, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 dp = dot_rows<D>(vs, 16 * t, gv, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + 16 * t + 4 * g + r;
+        const bool vis = key < N && !(CAUSAL && key > myq);
+        const float p = vis ? expf(s[r] * a.scale - lse) : 0.f;
+        dp[r] = p * (dp[r] - dvl);
       }
-      const float p = expf(s * a.scale - lse);
-      const float dsv = p * (dp - dvl);
-#pragma unroll
-      for (int c = 0; c < D; ++c) dq[c] = __builtin_fmaf(dsv, ks[j][c], dq[c]);
+      acc_tr<D>(dq, kt, 16 * t, dp);
     }
   }
-  if (myq < N) {
-    float* row = a.out0 + base + (int64_t)myq * rs;
-#pragma unroll
-    for (int c = 0; c < D; ++c) row[c] = dq[c] * a.scale;
-  }
+  if (myq < N) store_row<D>(a.out0 + base + (int64_t)myq * rs, dq, a.scale);
 }
 
 template <int D>
 hipError_t fwd(const F32Args& a, int BH, int causal, hipStream_t st) {
-  const dim3 grid(a.ntiles * BH), block(kRows);
+  const dim3 grid(a.ntiles * BH), block(kThreads);
   if (causal) hipLaunchKernelGGL((fwd_f32_kernel<D, true>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((fwd_f32_kernel<D, false>), grid, block, 0, st, a);
   return hipGetLastError();
@@ -254,17 +351,15 @@ hipError_t bwd(const F32Args& a, int B, int BH, int causal, hipStream_t st) {
                      a.o, a.dout, const_cast<float*>(a.dvec), a.H, a.N, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid(a.ntiles * BH), block(kRows);
-  F32Args a1 = a;   // dK/dV pass: out0 = dK, out1 = dV
-  if (causal) hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, true>), grid, block, 0, st, a1);
-  else hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, false>), grid, block, 0, st, a1);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  return e;
+  const dim3 grid(a.ntiles * BH), block(kThreads);
+  if (causal) hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, false>), grid, block, 0, st, a);
+  return hipGetLastError();
 }
 
 template <int D>
 hipError_t bwd_dq(const F32Args& a, int BH, int causal, hipStream_t st) {
-  const dim3 grid(a.ntiles * BH), block(kRows);
+  const dim3 grid(a.ntiles * BH), block(kThreads);
   if (causal) hipLaunchKernelGGL((bwd_dq_f32_kernel<D, true>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((bwd_dq_f32_kernel<D, false>), grid, block, 0, st, a);
   return hipGetLastError();
