@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (FaError, LIB_PATH, fa_backward, fa_backward_cross, fa_backward_dkdv,  # noqa: F401
+from ._lib import (FaError, LIB_PATH, SYNC_CHECK_LIB_PATH, use_library, fa_backward, fa_backward_cross, fa_backward_dkdv,  # noqa: F401
                    fa_backward_dq, fa_backward_dqdkdv,
                    fa_backward_preprocess, fa_backward_workspace_bytes, fa_decode,
                    fa_decode_splits, fa_decode_workspace_bytes, fa_forward, fa_forward_cross,

@@ -7,6 +7,7 @@ library is missing or a call fails, an exception says so.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -14,10 +15,15 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
+# The race-detection build of the same sources and C ABI (-DFA_SYNC_CHECK):
+# every LDS read and global -> LDS copy completes at once, every barrier
+# drains all memory operations first; results must equal libfa.so's bit for bit.
+SYNC_CHECK_LIB_PATH = os.path.join(_HERE, "libfa_synccheck.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH, FA_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 
-_lib = None
+_libs = {}            # path -> loaded CDLL
+_active = None        # path the wrappers call; None = LIB_PATH
 
 
 class FaError(RuntimeError):
@@ -26,16 +32,18 @@ class FaError(RuntimeError):
         super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
 
 
-def load() -> ctypes.CDLL:
-    """Load libfa.so once; raise if it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the library the wrappers call (libfa.so unless use_library()
+    says otherwise), or the one at `path`, once; raise if it is not built."""
+    path = path or _active or LIB_PATH
+    lib = _libs.get(path)
+    if lib is not None:
+        return lib
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_39_amd.build` "
+            f"{path} is missing: build it with `python -m exact_io_aware_39_amd.build` "
             "(there is no non-HIP implementation)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     fwd_args = [P, P, P, P, P, I, I, I, I, F, I, P]
     bwd_args = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P]
@@ -78,8 +86,21 @@ def load() -> ctypes.CDLL:
     lib.fa_forward_fp8_workspace_bytes.restype = S
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
-    _lib = lib
+    _libs[path] = lib
     return lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Inside the block every wrapper calls the library at `path` (another
+    build of the same C ABI, e.g. SYNC_CHECK_LIB_PATH) instead of libfa.so."""
+    global _active
+    load(path)
+    prev, _active = _active, path
+    try:
+        yield
+    finally:
+        _active = prev
 
 
 def fa_status_string(status: int) -> str:

@@ -5,6 +5,13 @@
 Every source under csrc/ is compiled for gfx950 only.  Packed-fp32 VALU
 instructions are disabled (-packed-fp32-ops): the kernels are written in
 scalar fp32 for the softmax arithmetic.
+
+The same sources are also built with -DFA_SYNC_CHECK into
+libfa_synccheck.so, the race-detection build: every asm-issued LDS read and
+every global -> LDS copy completes at once and every workgroup barrier drains
+all memory operations first (csrc/fa_common.hpp).  It exports the same C ABI
+and must give bit-identical results; tests/test_gpu_sync_check.py compares
+the two.
 """
 from __future__ import annotations
 
@@ -17,6 +24,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa.so")
+OUT_SYNC_CHECK = os.path.join(PKG, "libfa_synccheck.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -47,8 +55,8 @@ def _sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src, obj, verbose):
-    cmd = [_hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def _compile(src, obj, verbose, extra=()):
+    cmd = [_hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -73,34 +81,51 @@ def _device_asm(src, out, verbose):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source, check the asm-issued LDS reads in the generated
-    assembly, and link libfa.so next to this file; returns its path."""
-    from . import asm_check
-
-    objdir = os.path.join(PKG, "_build")
-    os.makedirs(objdir, exist_ok=True)
-    srcs = _sources()
-    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
-    hips = [s for s in srcs if s.endswith(".hip")]
-    asms = [os.path.join(objdir, os.path.basename(s) + ".s") for s in hips]
-    jobs = [(_compile, so, ob) for so, ob in zip(srcs, objs)] + [(_device_asm, so, a) for so, a in zip(hips, asms)]
-    workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(workers) as ex:
-        list(ex.map(lambda j: j[0](j[1], j[2], verbose), jobs))
-    problems = []
-    for a in asms:
-        problems += asm_check.check_file(a)[0]
-    if problems:
-        raise RuntimeError("asm-issued LDS reads used before their wait:\n" + "\n".join(problems[:20]))
-    tmp = OUT + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, sync_check: bool = True) -> str:
+    """Compile every source, check the asm-issued LDS reads in the generated
+    assembly, and link libfa.so next to this file (and, with `sync_check`,
+    the sync-check build libfa_synccheck.so); returns the path of libfa.so."""
+    from . import asm_check
+    objdir = os.path.join(PKG, "_build")
+    syncdir = os.path.join(PKG, "_build", "sync_check")
+    os.makedirs(syncdir, exist_ok=True)
+    srcs = _sources()
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    sync_objs = [os.path.join(syncdir, os.path.basename(s) + ".o") for s in srcs]
+    hips = [s for s in srcs if s.endswith(".hip")]
+    asms = [os.path.join(objdir, os.path.basename(s) + ".s") for s in hips]
+    jobs = [(_compile, so, ob, ()) for so, ob in zip(srcs, objs)]
+    jobs += [(_device_asm, so, a, None) for so, a in zip(hips, asms)]
+    if sync_check:
+        jobs += [(_compile, so, ob, ("-DFA_SYNC_CHECK",)) for so, ob in zip(srcs, sync_objs)]
+    workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
+
+    def run(j):
+        f, src, out, extra = j
+        return f(src, out, verbose) if extra is None else f(src, out, verbose, extra)
+
+    with cf.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(run, jobs))
+    problems = []
+    for a in asms:
+        problems += asm_check.check_file(a)[0]
+    if problems:
+        raise RuntimeError("asm-issued LDS reads used before their wait:\n" + "\n".join(problems[:20]))
+    _link(objs, OUT, verbose)
+    if sync_check:
+        _link(sync_objs, OUT_SYNC_CHECK, verbose)
     return OUT
 
 

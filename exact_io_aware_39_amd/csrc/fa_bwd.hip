@@ -383,7 +383,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
     constexpr int MODE = decltype(mode_tag)::value;
     char* slot = smem + (s & 1) * SLOT;
     wait_vmem();
-    __syncthreads();
+    block_sync();
     if (s + 1 < nsteps) stage(s + 1, smem + ((s + 1) & 1) * SLOT);
     const int qi0 = qstart + s * kBq;
     if constexpr (MODE != 0) {
@@ -412,7 +412,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           dq_part[(wave * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + 32 * t + l32] = dqw[t][r];
-      __syncthreads();
+      block_sync();
 #pragma unroll
       for (int i = 0; i < 8 * D / 64; ++i) {
         const int idx = i * 64 + lane;
@@ -576,7 +576,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
   // general path.  Two loops, so that each body has one path (see dkdv_tile).
   auto step = [&](int t, auto full_tag) __attribute__((always_inline)) {
     wait_vmem();
-    __syncthreads();
+    block_sync();
     if (t + 1 < nkt) {
       stage_rows(a.k, t + 1, kbuf + ((t + 1) & 1) * TILE);
       stage_rows(a.v, t + 1, vbuf + ((t + 1) & 1) * TILE);

@@ -131,6 +131,37 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const FA_LDS char*)p;
 }
 
+// ---- Sync-check build
+// Built with -DFA_SYNC_CHECK (libfa_synccheck.so), every asm-issued LDS read
+// and every global/buffer -> LDS copy completes before the next instruction,
+// and every workgroup barrier first waits for all of the wave's memory
+// operations.  No barrier is added or moved: waves of one workgroup take
+// different paths in several kernels (ping-pong halves, per-wave causal
+// skips), so a barrier anywhere else could deadlock.  The arithmetic is
+// unchanged, so kernels whose ordering is right give bit-identical results in
+// both builds; a tile read before its copy landed, a copy that overwrites a
+// buffer another wave still reads, or an asm read used before its wait shows
+// as a difference (the check build lands every copy at once and never leaves
+// a read in flight).
+#ifdef FA_SYNC_CHECK
+constexpr bool kSyncCheck = true;
+#define FA_SYNC_CHECK_LDS_WAIT "\n\ts_waitcnt lgkmcnt(0)"
+#else
+constexpr bool kSyncCheck = false;
+#define FA_SYNC_CHECK_LDS_WAIT ""
+#endif
+__device__ __forceinline__ void sync_check_drain() {
+  if constexpr (kSyncCheck) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+}
+__device__ __forceinline__ void sync_check_copy_done() {
+  if constexpr (kSyncCheck) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+// Workgroup barrier (__syncthreads; in the sync-check build after a full drain).
+__device__ __forceinline__ void block_sync() {
+  sync_check_drain();
+  __syncthreads();
+}
+
 // ---- LDS reads issued from inline asm
 // The compiler treats the transposing-read builtin as a possible reader of
 // every global -> LDS copy still in flight and drains them all (vmcnt(0))
@@ -149,13 +180,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <uint32_t OFF>
 __device__ __forceinline__ s16x4 lds_tr16_issue(uint32_t addr) {
   s16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" FA_SYNC_CHECK_LDS_WAIT : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
 }
 template <uint32_t OFF>
 __device__ __forceinline__ bf16x8 lds_b128_issue(uint32_t addr) {
   bf16x8 r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" FA_SYNC_CHECK_LDS_WAIT : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
 }
 template <int N>
@@ -183,6 +214,7 @@ __device__ __forceinline__ bf16x8 tr_pair_take(s16x4 (&r)[2]) {
 // for every lane of the wave.  Completion is tracked by vmcnt.
 __device__ __forceinline__ void global_to_lds16(const void* src, void* lds_block) {
   __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)lds_block, 16, 0, 0);
+  sync_check_copy_done();
 }
 
 // Buffer descriptor over `bytes` bytes from `base` (raw, unswizzled dwords);
@@ -195,11 +227,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // `voff` of the buffer land at lds_block + 16 l (lds_block wave-uniform).
 __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* lds_block) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds_block, 16, voff, 0, 0, 0);
+  sync_check_copy_done();
 }
 
 // Asynchronous 4-byte buffer -> LDS copy: lane l's dword lands at lds_block + 4 l.
 __device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* lds_block) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds_block, 4, voff, 0, 0, 0);
+  sync_check_copy_done();
 }
 
 // Wait until this wave's global loads (including global -> LDS copies) are done.

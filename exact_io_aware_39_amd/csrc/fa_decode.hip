@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void decode_split_kernel(De
 
   // ---- merge the four waves through LDS (the rings are no longer needed)
   const float lsum = sum_halves(l_part);
-  __syncthreads();
+  block_sync();
   float* mm = reinterpret_cast<float*>(smem);            // [wave][32] running max
   float* ll = mm + kDecWaves * 32;                       // [wave][32] running sum
   float* oo = reinterpret_cast<float*>(smem + 2048);     // [wave][32][D] unnormalised O
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void decode_split_kernel(De
       *reinterpret_cast<f32x4*>(oo + (wave * 32 + l32) * D + d0) =
           (f32x4){oacc[t][4 * g4 + 0], oacc[t][4 * g4 + 1], oacc[t][4 * g4 + 2], oacc[t][4 * g4 + 3]};
     }
-  __syncthreads();
+  block_sync();
   // Thread (q, part): query q = tid / 8, dims part, part + 8, ...
   const int q = tid >> 3, part = tid & 7;
   if (q < Nq) {

@@ -169,10 +169,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
 
   const int kend = CAUSAL ? min(N, tile * kRows + kRows) : N;
   for (int k0 = 0; k0 < kend; k0 += kTile) {
-    __syncthreads();
+    block_sync();
     stage<D>(a.k, base, rs, k0, N, ks, nullptr);
     stage<D>(a.v, base, rs, k0, N, nullptr, vt);
-    __syncthreads();
+    block_sync();
     if (CAUSAL && k0 > qw + 15) continue;   // the whole stage is above this wave's diagonal
     f32x4 s[kTile / 16];
     float mx = -INFINITY;
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(F32Args a) {
 
   const int qstart = CAUSAL ? tile * kRows : 0;   // earlier queries see none of these keys
   for (int i0 = qstart; i0 < N; i0 += kTile) {
-    __syncthreads();
+    block_sync();
     stage<D>(a.q, base, rs, i0, N, qs, qt);
     stage<D>(a.dout, base, rs, i0, N, gs, gt);
     if (threadIdx.x < kTile) {
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(F32Args a) {
       ls[threadIdx.x] = qi < N ? lse[qi] : 0.f;
       dd[threadIdx.x] = qi < N ? dvec[qi] : 0.f;
     }
-    __syncthreads();
+    block_sync();
     if (CAUSAL && i0 + kTile - 1 < kw) continue;   // no query of the stage sees this wave's keys
 #pragma unroll
     for (int u = 0; u < kTile / 16; ++u) {
@@ -314,10 +314,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(F32Args a) {
 
   const int kend = CAUSAL ? min(N, tile * kRows + kRows) : N;
   for (int k0 = 0; k0 < kend; k0 += kTile) {
-    __syncthreads();
+    block_sync();
     stage<D>(a.k, base, rs, k0, N, ks, kt);
     stage<D>(a.v, base, rs, k0, N, vs, nullptr);
-    __syncthreads();
+    block_sync();
     if (CAUSAL && k0 > qw + 15) continue;
 #pragma unroll
     for (int t = 0; t < kTile / 16; ++t) {

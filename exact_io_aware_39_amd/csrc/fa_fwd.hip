@@ -384,6 +384,7 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), (fwd_waves<
     // flight; the memory clobber keeps LDS accesses on their side.
     auto phase_end = [] {
       __builtin_amdgcn_sched_barrier(0);
+      sync_check_drain();
       asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -413,6 +414,7 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), (fwd_waves<
     auto phase_end_publish = [&] __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
       wait_vmem_n<2 * CPW>();
+      sync_check_drain();
       asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -499,7 +501,7 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), (fwd_waves<
         CAUSAL ? min((qw0 + qoff + 1) / kBc, Nk / kBc) : Nk / kBc);
     stage_rows(Kg, 0, kbuf);
     wait_vmem();
-    __syncthreads();
+    block_sync();
     stage_or_skip(Kg, 1, kbuf + TILE);
     stage_or_skip(Vg, 0, vbuf);
     // Half B starts one phase late (phase 0 idle); the sections below keep
@@ -555,13 +557,13 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), (fwd_waves<
       const int cur = cur_tag;
       if constexpr (NB == 3) {
         wait_vmem_n<2 * CPW>();
-        __syncthreads();
+        block_sync();
         const int nxt = cur == 0 ? 2 : cur - 1;   // (cur + 2) % 3
         stage_or_skip(Kg, kt + 2, kbuf + nxt * TILE);
         stage_or_skip(Vg, kt + 2, vbuf + nxt * TILE);
       } else {
         wait_vmem();
-        __syncthreads();
+        block_sync();
         if (kt + 1 < nkt) {
           stage_rows(Kg, kt + 1, kbuf + (cur ^ 1) * TILE);
           stage_rows(Vg, kt + 1, vbuf + (cur ^ 1) * TILE);

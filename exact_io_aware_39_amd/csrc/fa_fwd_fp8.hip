@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void fp8_vt_kernel(const uint8_t* __restrict__
 #pragma unroll
     for (int j = 0; j < 4; ++j) tile[row][4 * ch + j] = x[j];
   }
-  __syncthreads();
+  block_sync();
   uint8_t* dst = vt + (int64_t)bh * D * Nkp + k0;
   for (int c = threadIdx.x; c < D * 4; c += 256) {
     const int d = c >> 2, kc = c & 3;   // row d of V^T, keys 16 kc .. 16 kc + 15
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(64 * kF8Waves, (D == 128 ? 3 : 4)) void fwd_fp8_ker
   auto step = [&](int kt, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
     const int cur = buf_tag;
     wait_vmem();
-    __syncthreads();
+    block_sync();
     if (kt + 1 < nkt) stage(kt + 1, cur ^ 1);
     const int k0 = kt * kF8Bc;
     if (CAUSAL && k0 > qw0 + qoff + 31) return;   // no key of the tile is visible to this wave

@@ -93,6 +93,27 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_sync_check_build_exports_the_same_abi():
+    """libfa_synccheck.so (the race-detection build) exports every declared
+    entry point too, and its host checks agree with libfa.so's."""
+    path = os.path.join(ROOT, "exact_io_aware_39_amd", "libfa_synccheck.so")
+    if not os.path.exists(path):
+        pytest.fail("libfa_synccheck.so not built: run python -m exact_io_aware_39_amd.build")
+    sc = ctypes.CDLL(path)
+    for name in declared_functions():
+        assert hasattr(sc, name), name
+    sc.fa_backward_workspace_bytes.argtypes = [ctypes.c_int] * 4
+    sc.fa_backward_workspace_bytes.restype = ctypes.c_size_t
+    sc.fa_status_string.argtypes = [ctypes.c_int]
+    sc.fa_status_string.restype = ctypes.c_char_p
+    normal = ctypes.CDLL(LIB)
+    normal.fa_backward_workspace_bytes.argtypes = [ctypes.c_int] * 4
+    normal.fa_backward_workspace_bytes.restype = ctypes.c_size_t
+    for shape in ((1, 1, 1, 64), (2, 3, 300, 128), (1, 2, 600, 256)):
+        assert sc.fa_backward_workspace_bytes(*shape) == normal.fa_backward_workspace_bytes(*shape)
+    assert sc.fa_status_string(4).startswith(b"FA_ERR_SCRATCH_LIMIT")
+
+
 def _fwd(lib, name="fa_forward", ptrs=(P, P, P, P, P), B=1, H=1, N=128, d=64, scale=0.125, causal=0):
     return getattr(lib, name)(*ptrs, B, H, N, d, scale, causal, None)
 
