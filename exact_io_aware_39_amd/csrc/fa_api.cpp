@@ -60,15 +60,18 @@ fa_status check_decode(int B, int H, int Nq, int Nk, int d, float scale, int cau
   return FA_OK;
 }
 
-// Keep threshold floor(p 2^32) and scale 1 / (1 - p) of a dropout rate in [0, 1).
+// 16-bit keep threshold t = round(p 2^16) (ties to even, at most 2^16 - 1)
+// of a dropout rate in [0, 1), and the scale 2^16 / (2^16 - t) of kept
+// probabilities (the inverse of the keep probability 1 - t 2^-16).
 fa::DropParams drop_params(float p, uint64_t seed, uint32_t offset) {
   fa::DropParams dp;
   dp.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
   dp.key1 = (uint32_t)(seed >> 32);
   dp.offset = offset;
-  const double t = std::floor((double)p * 4294967296.0);
-  dp.thr = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
-  dp.inv_keep = (float)(1.0 / (1.0 - (double)p));
+  const double r = std::nearbyint((double)p * 65536.0);   // default rounding: to nearest, ties to even
+  const uint32_t t = r >= 65535.0 ? 65535u : (uint32_t)r;
+  dp.thr = t << 16;
+  dp.inv_keep = (float)(65536.0 / (double)(65536u - t));
   return dp;
 }
 

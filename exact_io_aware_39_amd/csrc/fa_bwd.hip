@@ -289,6 +289,12 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
   auto update = [&](auto mask_tag, const char* slot, int sb, const f32x16& sacc, const f32x16& pacc, int qi0)
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    // Keep bits of this lane's 16 rows of the block (bit 4 g4 + e: row qi0 +
+    // 8 g4 + 4 hh + e); lane l32 holds key kw0 + l32 with kw0 % 32 == 0.  (At
+    // D = 256 the DPP exchange makes this ROCm 7.2 compiler crash in its AGPR
+    // rewrite pass; that head size draws each element on its own.)
+    uint32_t dbits = 0;
+    if constexpr (DROP && D <= 128) dbits = drop_bits16(a.drop, bh, mykey, qi0 + 4 * hh);
     // Query rows 16 u .. 16 u + 15 of the tile (registers 8u .. 8u+7) at a time.
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -301,12 +307,9 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
         float zq[4];
         if constexpr (DROP) {
           nd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (32 * sb + 8 * g4 + 4 * hh) * 4);
-          // lane l32 holds key kw0 + l32 (kw0 % 4 == 0), so each quad holds
-          // four consecutive keys of the same rows.  (At D = 256 the quad
-          // exchange makes this ROCm 7.2 compiler crash in its AGPR rewrite
-          // pass; that head size draws each element on its own.)
           if constexpr (D <= 128) {
-            drop_mult_quad(a.drop, bh, qi0 + 8 * g4 + 4 * hh, mykey, zq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zq[e] = drop_bit_mult(dbits, 4 * g4 + e, a.drop.inv_keep);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) zq[e] = drop_mult1(a.drop, bh, qi0 + 8 * g4 + 4 * hh + e, mykey);
@@ -540,12 +543,9 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float ds[8];
-      float z[2][4];
-      if constexpr (DROP) {
-        // registers 8 u + 4 g + e: keys k0 + 32 j + 8 (2 u + g) + 4 hh + e
-#pragma unroll
-        for (int g = 0; g < 2; ++g) drop_mult4(a.drop, bh, myq, k0 + 32 * j + 8 * (2 * u + g) + 4 * hh, z[g]);
-      }
+      float z[8];
+      // registers 8 u + e: keys k0 + 32 j + 16 u + 4 hh + 8 (e >> 2) + (e & 3), one call
+      if constexpr (DROP) drop_mult8(a.drop, bh, myq, k0 + 32 * j + 16 * u + 4 * hh, z);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * u + e;
@@ -556,7 +556,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
           pv = hide ? 0.f : pv;
         }
         if constexpr (DROP) {
-          const float zz = z[e >> 2][e & 3];
+          const float zz = z[e];
           ds[e] = pv * __builtin_fmaf(zz, pacc[r], (1.f - zz) * ndval);
         } else {
           ds[e] = pv * pacc[r];

@@ -285,12 +285,14 @@ __device__ __forceinline__ void tile_of(int id, int ntiles, int bhcount, bool ca
 }
 
 // ---- dropout on the probabilities
-// The mask is recomputed wherever it is needed, never stored: element (query
-// row i, key j) of head bh uses word j % 4 of Philox4x32-10 (J. K. Salmon et
-// al., "Parallel random numbers: as easy as 1, 2, 3", SC 2011) on the counter
-// (j / 4, i, bh, offset) under the 64-bit seed as key, and is kept when that
-// word is >= thr = floor(p 2^32); a kept probability is scaled by 1 / (1 - p).
-// (DropParams is declared with the launchers.)
+// The mask is recomputed wherever it is needed, never stored.  Each call of
+// Philox4x32-10 (J. K. Salmon et al., "Parallel random numbers: as easy as 1,
+// 2, 3", SC 2011) under the 64-bit seed as key yields eight 16-bit fields
+// (field f: the low half of word f / 2 for even f, the high half for odd f).
+// Element (query row i, key j) of head bh is field 4 ((j >> 3) & 1) + (j & 3)
+// of the call on the counter (2 (j >> 4) + ((j >> 2) & 1), i, bh, offset), and
+// is kept when that field is >= t = round(p 2^16); a kept probability is
+// scaled by 2^16 / (2^16 - t).  (DropParams is declared with the launchers.)
 
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
                                                uint32_t k0, uint32_t k1) {
@@ -310,40 +312,73 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_
   return (u32x4){x0, x1, x2, x3};
 }
 
-// Multipliers (0 or 1 / (1 - p)) of keys key4 .. key4 + 3 (key4 % 4 == 0) of
-// query row `row` in head bh: one generator call.
-__device__ __forceinline__ void drop_mult4(const DropParams& dp, int bh, int row, int key4, float (&z)[4]) {
-  const u32x4 w = philox4x32_10((uint32_t)key4 >> 2, (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) z[e] = w[e] >= dp.thr ? dp.inv_keep : 0.f;
+// Counter word 0 of key j: one call serves the 8 keys j0 + {0..3, 8..11}
+// (j0 % 16 in {0, 4}) of one row, key j0 + 8 (f >> 2) + (f & 3) taking field f.
+__device__ __forceinline__ uint32_t drop_ctr0(uint32_t j) { return ((j >> 4) << 1) | ((j >> 2) & 1u); }
+
+// Whether field F of a generator output is kept, against thr = t << 16: the
+// low half of a word is compared shifted up, the high half in place (the low
+// bits under it cannot lift it past a multiple of 2^16).
+template <int F>
+__device__ __forceinline__ bool drop_keep(const u32x4& w, uint32_t thr) {
+  if constexpr ((F & 1) != 0) return w[F >> 1] >= thr;
+  else return (w[F >> 1] << 16) >= thr;
+}
+
+// Multipliers (0 or inv_keep) of keys j0 + 8 (f >> 2) + (f & 3), f = 0..7,
+// of query row `row` in head bh (j0 % 16 in {0, 4}): one generator call.
+__device__ __forceinline__ void drop_mult8(const DropParams& dp, int bh, int row, int j0, float (&z)[8]) {
+  const u32x4 w = philox4x32_10(drop_ctr0((uint32_t)j0), (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
+  static_for<0, 8>([&](auto F) { z[decltype(F)::value] = drop_keep<decltype(F)::value>(w, dp.thr) ? dp.inv_keep : 0.f; });
 }
 
 // Multiplier of one element (query row `row`, key `key`) of head bh.
 __device__ __forceinline__ float drop_mult1(const DropParams& dp, int bh, int row, int key) {
-  const u32x4 w = philox4x32_10((uint32_t)key >> 2, (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
-  const int e = key & 3;
-  const uint32_t x = e == 0 ? w[0] : e == 1 ? w[1] : e == 2 ? w[2] : w[3];
-  return x >= dp.thr ? dp.inv_keep : 0.f;
+  const u32x4 w = philox4x32_10(drop_ctr0((uint32_t)key), (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
+  const int f = ((key >> 1) & 4) | (key & 3);
+  const uint32_t x = (f >> 1) == 0 ? w[0] : (f >> 1) == 1 ? w[1] : (f >> 1) == 2 ? w[2] : w[3];
+  return ((f & 1) ? x : (x << 16)) >= dp.thr ? dp.inv_keep : 0.f;
 }
 
-// Multipliers of rows row0 .. row0 + 3 at this lane's key, for layouts where
-// the four lanes of each DPP quad (lanes 4m .. 4m+3, all active) hold keys
-// 4n .. 4n+3 in lane order and the same four rows.  One generator call per
-// lane instead of four: the lane at quad position q draws the four keys of
-// row row0 + q, the quad pools its 16 keep bits (bit 4 e + j: row e, key j)
-// with two DPP exchanges, and every lane takes bit 4 e + q of each row e.
-__device__ __forceinline__ void drop_mult_quad(const DropParams& dp, int bh, int row0, int key, float (&z)[4]) {
-  const int q = key & 3;
-  const u32x4 w = philox4x32_10((uint32_t)key >> 2, (uint32_t)(row0 + q), (uint32_t)bh, dp.offset, dp.key0, dp.key1);
-  uint32_t bits = 0;
+// Keep bits of 16 query rows at this lane's key, for layouts where lane l
+// holds key kb + l % 32 (kb % 32 == 0) and the rows row0 + 8 (r >> 2) +
+// (r & 3), r = 0..15, the same in every lane of a half-wave: bit r of the
+// result is the keep bit of row r.  The 8 lanes whose keys share a generator
+// call (lane bits 0, 1 and 3 vary; the lane at position p = 4 bit3 + 2 bit1 +
+// bit0 holds field p) draw two calls each: position p the rows 2p and 2p + 1,
+// 8 keep bits apiece, packed as the 2-bit entry (row 2p, row 2p + 1) of key q
+// at bits 2q, 2q + 1.  Three exchanges with lanes l ^ 1, l ^ 2 and l ^ 8
+// (DPP; every lane of the wave must be active) transpose that 8 x 8 matrix of
+// entries, one index bit per exchange, so each lane ends with the entries of
+// its own key: two calls per lane per 16 rows instead of 16.
+__device__ __forceinline__ uint32_t drop_bits16(const DropParams& dp, int bh, int key, int row0) {
+  const int pos = ((key >> 1) & 4) | (key & 3);
+  const uint32_t c0 = drop_ctr0((uint32_t)key);
+  uint32_t m = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bits |= (w[j] >= dp.thr ? 1u : 0u) << j;
-  bits <<= 4 * q;
-  // quad_perm [1,0,3,2] then [2,3,0,1]: OR over the four lanes of the quad.
-  bits |= (uint32_t)__builtin_amdgcn_mov_dpp((int)bits, 0xB1, 0xF, 0xF, false);
-  bits |= (uint32_t)__builtin_amdgcn_mov_dpp((int)bits, 0x4E, 0xF, 0xF, false);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) z[e] = (bits >> (4 * e + q)) & 1u ? dp.inv_keep : 0.f;
+  for (int t = 0; t < 2; ++t) {
+    const int r = 2 * pos + t;
+    const u32x4 w = philox4x32_10(c0, (uint32_t)(row0 + 8 * (r >> 2) + (r & 3)), (uint32_t)bh, dp.offset,
+                                  dp.key0, dp.key1);
+    static_for<0, 8>([&](auto F) {
+      constexpr int f = decltype(F)::value;
+      m |= drop_keep<f>(w, dp.thr) ? (1u << (2 * f + t)) : 0u;
+    });
+  }
+  // Stage s: bit s of the position and bit s of the entry index trade places.
+  auto stage = [&](uint32_t y, int s, uint32_t hi_mask, int sh) __attribute__((always_inline)) {
+    return ((pos >> s) & 1) ? (m & hi_mask) | ((y & hi_mask) >> sh) : (m & ~hi_mask) | ((y & ~hi_mask) << sh);
+  };
+  m = stage((uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false), 0, 0xCCCCu, 2);    // lane ^ 1
+  m = stage((uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false), 1, 0xF0F0u, 4);    // lane ^ 2
+  m = stage((uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x128, 0xF, 0xF, false), 2, 0xFF00u, 8);   // lane ^ 8 (row_ror:8)
+  return m;
+}
+
+// Multiplier of keep bit r of a drop_bits16 result (0 or inv_keep).
+__device__ __forceinline__ float drop_bit_mult(uint32_t bits, int r, float inv_keep) {
+  const uint32_t all = (uint32_t)((int32_t)(bits << (31 - r)) >> 31);
+  return __uint_as_float(all & __float_as_uint(inv_keep));
 }
 
 }  // namespace fa

@@ -237,13 +237,14 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), (fwd_waves<
         lsum[r & 1] += e;
       }
       if constexpr (DROP) {
-        // registers 4 g .. 4 g + 3: keys k0 + 32 j + 8 g + 4 hh + 0..3
+        // register 4 g + e holds key k0 + 32 j + 8 g + 4 hh + e; one call
+        // serves registers 8 c .. 8 c + 7 (groups g = 2c, 2c + 1)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float z[4];
-          drop_mult4(a.drop, bh, myq, k0 + 32 * j + 8 * g + 4 * hh, z);
+        for (int c = 0; c < 2; ++c) {
+          float z[8];
+          drop_mult8(a.drop, bh, myq, k0 + 32 * j + 16 * c + 4 * hh, z);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) p[4 * g + e] *= z[e];
+          for (int f = 0; f < 8; ++f) p[8 * c + f] *= z[f];
         }
       }
 #pragma unroll

@@ -25,14 +25,16 @@ size_t fwd_fp8_workspace_bytes(int B, int H, int Nk, int d);
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, float dq, float dk, float dv,
                           void* o, float* lse, void* ws, const AttnShape& s, int Nk, hipStream_t stream);
 // Dropout on the probabilities: element (query row i, key j) of head bh is
-// kept when word j % 4 of Philox4x32-10 on the counter (j / 4, i, bh, offset)
-// under the key (key0, key1) is >= thr; kept probabilities are scaled by
-// inv_keep = 1 / (1 - p).
+// kept when 16-bit field 4 ((j >> 3) & 1) + (j & 3) (field f: the low half of
+// word f / 2 for even f, the high half for odd f) of Philox4x32-10 on the
+// counter (2 (j >> 4) + ((j >> 2) & 1), i, bh, offset) under the key
+// (key0, key1) is >= t = round(p 2^16); kept probabilities are scaled by
+// inv_keep = 2^16 / (2^16 - t).
 struct DropParams {
   uint32_t key0, key1;   // seed, low and high word
   uint32_t offset;       // fourth counter word (one mask per offset)
-  uint32_t thr;          // floor(p 2^32)
-  float inv_keep;        // 1 / (1 - p)
+  uint32_t thr;          // t << 16 (a field f is kept when f << 16 >= thr)
+  float inv_keep;        // 2^16 / (2^16 - t)
 };
 // Forward with dropout (square attention).
 hipError_t launch_fwd_dropout_bf16(const void* q, const void* k, const void* v, void* o, float* lse,

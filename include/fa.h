@@ -98,11 +98,16 @@ fa_status fa_forward_cross(const void* Q, const void* K, const void* V, void* O,
  * Forward with dropout on the probabilities, bfloat16 tensors (page "知识点13 |
  * FlashAttention深度攻略", section 7: the softmax step fused into the one
  * kernel carries the mask and dropout).  O = (P * Z) V with P the softmax of
- * scale Q K^T [+ causal mask] and Z_ij = keep_ij / (1 - p_drop); LSE is that
- * of P (unchanged by dropout).  The mask is never stored: element (query row
- * i, key j) of head b*H + h is kept when word j % 4 of Philox4x32-10
- * (Salmon et al., SC 2011) on the counter (j / 4, i, b*H + h, offset) under
- * the key (seed mod 2^32, seed / 2^32) is >= floor(p_drop 2^32).
+ * scale Q K^T [+ causal mask] and Z_ij = keep_ij * 2^16 / (2^16 - t),
+ * t = round(p_drop 2^16) (ties to even, at most 2^16 - 1: the drop rate is
+ * p_drop to the nearest multiple of 2^-16, and the scale is the inverse of
+ * the keep probability); LSE is that of P (unchanged by dropout).  The mask
+ * is never stored: each call of Philox4x32-10 (Salmon et al., SC 2011) under
+ * the key (seed mod 2^32, seed / 2^32) yields eight 16-bit fields (field f:
+ * the low half of word f / 2 for even f, the high half for odd f); element
+ * (query row i, key j) of head b*H + h is kept when field
+ * 4 ((j / 8) % 2) + j % 4 of the call on the counter
+ * (2 (j / 16) + (j / 4) % 2, i, b*H + h, offset) is >= t.
  * 0 <= p_drop < 1 (else FA_ERR_INVALID_ARG); p_drop = 0 keeps everything.
  * Same layouts, checks and limits as fa_forward (square attention).
  */

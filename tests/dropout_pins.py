@@ -5,8 +5,12 @@
     zero, all ones, and the digits of pi.
   * The mask keeps a fraction 1 - p of the elements (within 5 sigma of the
     binomial spread) for several p; p = 0 keeps everything; different seeds,
-    offsets and heads give different masks; element (i, j) is word j mod 4 of
-    one generator call per four keys (checked on single calls).
+    offsets and heads give different masks; element (i, j) is 16-bit field
+    4 (j div 8 mod 2) + j mod 4 of the call on counter word
+    2 (j div 16) + (j div 4 mod 2), computed here from single calls written
+    out per element; every field of a call serves exactly one key; the
+    threshold rounds p 2^16 to the nearest integer and the kept scale is
+    2^16 / (2^16 - threshold), checked on hand values.
   * p = 0 reduces forward and backward to plain attention (oracle.attention).
   * With the mask fixed, dQ, dK, dV agree with central finite differences of
     sum(O * dO), causal and not; sum_j dK_j = 0 and D = rowsum(dO * O) still
@@ -54,14 +58,33 @@ def pin_mask(drop):
                   drop.keep_mask(1, rows, 256, 0.5, seed=11, offset=1),
                   drop.keep_mask(2, rows, 256, 0.5, seed=11, offset=0)):
         assert 0.4 < np.mean(other != base) < 0.6, "masks of different seeds/offsets/heads agree"
+    # hand values of the threshold and the scale of kept probabilities
+    assert drop.threshold(0.0) == 0 and drop.threshold(0.5) == 32768
+    assert drop.threshold(0.1) == 6554            # 6553.6 rounds up
+    assert drop.threshold(0.25) == 16384 and drop.threshold(1 - 2 ** -20) == 65535
+    assert drop.keep_scale(0.5) == 2.0 and drop.keep_scale(0.75) == 4.0 and drop.keep_scale(0.0) == 1.0
+    assert abs(drop.keep_scale(0.1) - 65536 / 58982) < 1e-15
+    # element by element from single generator calls
     seed, bh, off, p = 0xDEADBEEFCAFE, 5, 9, 0.3
-    keep = drop.keep_mask(bh, np.array([0, 7, 41]), 23, p, seed=seed, offset=off)
-    thr = drop.threshold(p)
+    keep = drop.keep_mask(bh, np.array([0, 7, 41]), 45, p, seed=seed, offset=off)
+    thr = 19661                                    # round(0.3 * 65536) = round(19660.8)
+    assert drop.threshold(p) == thr
     for a, i in enumerate((0, 7, 41)):
-        for j in range(23):
-            w = drop.philox4x32_10(np.array([j // 4, i, bh, off], dtype=np.uint64),
-                                   (seed & 0xFFFFFFFF, seed >> 32))[j % 4]
-            assert keep[a, j] == (int(w) >= thr), f"element ({i}, {j})"
+        for j in range(45):
+            ctr0 = 2 * (j // 16) + (j // 4) % 2
+            field = 4 * ((j // 8) % 2) + j % 4
+            w = int(drop.philox4x32_10(np.array([ctr0, i, bh, off], dtype=np.uint64),
+                                       (seed & 0xFFFFFFFF, seed >> 32))[field // 2])
+            half = (w >> (16 * (field % 2))) & 0xFFFF
+            assert keep[a, j] == (half >= thr), f"element ({i}, {j})"
+    # one call serves keys 16a + 4b + {0..3, 8..11}: eight distinct fields
+    c, f = drop.counter_field(np.arange(256))
+    pairs = set(zip(c.tolist(), f.tolist()))
+    assert len(pairs) == 256 and set(f.tolist()) == set(range(8)), "keys share a field"
+    for a in range(16):
+        for b in range(2):
+            keys = [16 * a + 4 * b + e for e in (0, 1, 2, 3, 8, 9, 10, 11)]
+            assert set(c[keys].tolist()) == {2 * a + b} and sorted(f[keys].tolist()) == list(range(8))
 
 
 def _inputs(seed, n, d):

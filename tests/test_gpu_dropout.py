@@ -3,7 +3,7 @@
 The oracle replays the mask from (head, query row, key, seed, offset) with its
 own Philox4x32-10 (oracle/dropout.py), so the comparison is element by element
 against the same mask.  Bars: dropout multiplies every kept term by
-s = 1 / (1 - p), so outputs grow by up to s and so does the bf16 rounding of
+s = keep_scale(p) (about 1 / (1 - p)), so outputs grow by up to s and so does the bf16 rounding of
 them (half an ulp is up to 2^-9 |x|).  An element may differ from the oracle
 by 2^-8 |ref| (the rounding of the result, with margin) plus s times the
 plain path's absolute bar (2e-2); the mean error may reach s times the plain
@@ -28,7 +28,7 @@ def check(got, ref, p, what):
     got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
     assert np.isfinite(got).all(), f"{what}: non-finite values"
-    s = 1.0 / (1.0 - p)
+    s = drop.keep_scale(p)
     err = np.abs(got - ref)
     over = err - 2.0 ** -8 * np.abs(ref)
     assert over.max() <= BF16_MAX * s, f"{what}: max abs err {err.max():.3e} ({over.max():.3e} beyond 2^-8 |ref|)"

@@ -1,19 +1,19 @@
 """Bit-exact check of the dropout keep mask that each pass draws on the GPU.
 
-The mask is integer work (Philox4x32-10 words compared with floor(p 2^32)), so
-it is compared bit for bit with oracle.dropout.keep_mask, not through a float
-tolerance.  Inputs are chosen so that every kept or dropped element shows up
+The mask is integer work (16-bit fields of Philox4x32-10 outputs compared with
+round(p 2^16)), so it is compared bit for bit with oracle.dropout.keep_mask,
+not through a float tolerance.  Inputs are chosen so that every kept or dropped element shows up
 in its own output element (N <= d, Q = 0 so that every visible key of row i
 has the probability 1 / n_i, n_i = number of keys row i sees):
 
 * forward, V = identity (row j of V is e_j): O_ij = z_ij / n_i, which is
   exactly zero when key j of row i is dropped and at least 1 / N otherwise;
 * dK/dV pass, dO = identity: dV_ji = P_ij z_ij, again exactly zero when
-  dropped (this is the pass whose lanes share one generator call per four
-  keys at d <= 128);
+  dropped (this is the pass whose lanes trade keep bits across the 8 lanes
+  of one generator call at d <= 128);
 * dQ pass, V = all ones, dO = identity, K = identity: dP_ij = 1, so
   dS_ij = P_ij (z_ij - D_i) and dQ_ij = dS_ij; a kept element gives
-  P_i (s - D_i), a dropped one -P_i D_i (s = 1 / (1 - p), D_i read from the
+  P_i (s - D_i), a dropped one -P_i D_i (s = keep_scale(p), D_i read from the
   GPU's own O), two values s P_i apart, and the element is classified by the
   midpoint between them.
 
@@ -56,7 +56,7 @@ def _read_masks(B, H, N, d, causal, p, seed, offset):
     ones = torch.ones((B, N, H, d), dtype=torch.bfloat16, device="cuda")
     vis = _visible(N, causal)
     n = vis.sum(axis=1).astype(np.float64)              # keys seen by each row
-    s = float(np.float32(1.0 / (1.0 - p)))
+    s = float(np.float32(drop.keep_scale(p)))
 
     # forward and dK/dV pass: V = identity, dO = identity
     o, lse = fa.forward_dropout(zero, eye, eye, p, seed, offset, scale=scale, causal=causal)

@@ -11,7 +11,8 @@ def test_dropout_oracle_pin(pin):
     pin(drop)
 
 
-_orig = {n: getattr(drop, n) for n in ("philox4x32_10", "keep_mask", "forward", "backward", "threshold")}
+_orig = {n: getattr(drop, n) for n in ("philox4x32_10", "keep_mask", "forward", "backward", "threshold",
+                                      "keep_scale", "counter_field")}
 
 
 def _philox_wrong_multiplier(ctr, key):
@@ -36,13 +37,39 @@ def _mask_inverted(bh, rows, nk, p, seed, offset=0):
     return ~_orig["keep_mask"](bh, rows, nk, p, seed, offset) if p > 0 else _orig["keep_mask"](bh, rows, nk, p, seed, offset)
 
 
+def _mask_halves_swapped(bh, rows, nk, p, seed, offset=0):
+    """Reads the high 16 bits where the low ones are meant and vice versa."""
+    rows = np.asarray(rows, dtype=np.uint64)
+    c, f = drop.counter_field(np.arange(nk))
+    ctr = np.zeros((rows.size, nk, 4), dtype=np.uint64)
+    ctr[..., 0], ctr[..., 1], ctr[..., 2], ctr[..., 3] = c[None, :], rows[:, None], bh, offset
+    words = drop.philox4x32_10(ctr, (int(seed) & 0xFFFFFFFF, int(seed) >> 32)).astype(np.uint64)
+    word = np.take_along_axis(words, (f >> np.uint64(1)).astype(np.int64)[None, :, None].repeat(rows.size, 0), 2)[..., 0]
+    field = (word >> (np.uint64(16) * (np.uint64(1) - (f & np.uint64(1))))[None, :]) & np.uint64(0xFFFF)
+    return field >= np.uint64(drop.threshold(p))
+
+
+def _counter_field_per_4_keys(j):
+    """The old one-word-per-element layout: counter j div 4, field 2 (j mod 4)."""
+    j = np.asarray(j, dtype=np.uint64)
+    return j >> np.uint64(2), (j & np.uint64(3)) << np.uint64(1)
+
+
+def _threshold_floor(p):
+    return min(int(np.floor(float(p) * 65536.0)), 65535)
+
+
+def _scale_one_over_1_minus_p(p):
+    return 1.0 / (1.0 - float(p))
+
+
 def _forward_variant(kind):
     def forward(q, k, v, scale, causal, keep, p):
         pm, _, _, lse = drop.softmax_rows(drop.scores(q, k, scale, causal))
         if kind == "no_rescale":
             z = np.where(keep, 1.0, 0.0)
         else:
-            z = np.where(keep, 1.0 / (1.0 - p), 0.0)
+            z = np.where(keep, drop.keep_scale(p), 0.0)
         pz = pm * z
         if kind == "renormalised":
             pz = pz / np.maximum(pz.sum(axis=1, keepdims=True), 1e-300)
@@ -54,7 +81,7 @@ def _backward_variant(kind):
     def backward(q, k, v, do, scale, causal, keep, p):
         q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
         pm, _, _, _ = drop.softmax_rows(drop.scores(q, k, scale, causal))
-        z = np.where(keep, 1.0 / (1.0 - p), 0.0)
+        z = np.where(keep, drop.keep_scale(p), 0.0)
         dv = (pm * (1.0 if kind == "dv_unmasked" else z)).T @ do
         dp = (do @ v.T) * (1.0 if kind == "dp_unmasked" else z)
         dvec = (pm * dp).sum(axis=1)
@@ -67,6 +94,10 @@ MUTANTS = {
     "philox_wrong_multiplier": ("philox4x32_10", _philox_wrong_multiplier),
     "mask_rows_and_keys_swapped": ("keep_mask", _mask_rows_keys_swapped),
     "mask_keeps_the_dropped": ("keep_mask", _mask_inverted),
+    "mask_16_bit_halves_swapped": ("keep_mask", _mask_halves_swapped),
+    "counter_and_field_of_the_old_layout": ("counter_field", _counter_field_per_4_keys),
+    "threshold_rounded_down": ("threshold", _threshold_floor),
+    "scale_not_from_the_threshold": ("keep_scale", _scale_one_over_1_minus_p),
     "forward_without_1_over_keep": ("forward", _forward_variant("no_rescale")),
     "forward_renormalised_after_dropout": ("forward", _forward_variant("renormalised")),
     "backward_dP_unmasked": ("backward", _backward_variant("dp_unmasked")),
