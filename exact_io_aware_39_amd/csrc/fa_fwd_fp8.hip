@@ -11,8 +11,9 @@
 //    The K rows of a 64-key tile are fed to the A operand in a permuted order,
 //    so that the 32 scores a lane holds are 32 consecutive keys (lane l holds
 //    query l % 32 and keys 32 (l / 32) .. 32 (l / 32) + 31 of the tile).
-//  * O^T += V^T P^T: P = 2^8 exp(S - m) (m the exact running row maximum, so
-//    2^8 p <= 256 < 448) is rounded to e4m3 and those 32 consecutive keys are
+//  * O^T += V^T P^T: P = 2^8 exp(S - m) (m a reference at most 0.75 below
+//    the running row maximum in log2 units, so 2^8 p <= 2^8.75 < 448, the
+//    largest e4m3 value) is rounded to e4m3 and those 32 consecutive keys are
 //    the lane's B operand as they stand; V^T comes from a transposed copy of V
 //    ([B H, d, Nk rounded up to 64], made by a pre-pass kernel), so that the A
 //    operand is 32 contiguous bytes of a V^T row.
@@ -35,6 +36,10 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 constexpr int kF8Bc = 64;         // keys per step
 constexpr int kF8Waves = 4;       // waves per workgroup, 32 query rows each
 constexpr float kF8PLog2 = 8.0f;  // p is rounded as 2^8 p
+// The reference max moves only when some row's max exceeds it by more than
+// this (log2 units): then 2^8 p <= 2^8.75 < 448, the largest e4m3 value, so
+// no probability overflows, and most steps skip the rescale of O.
+constexpr float kF8Slack = 0.75f;
 
 struct Fp8Args {
   const uint8_t* q;
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(64 * kF8Waves, (D == 128 ? 3 : 4)) void fwd_fp8_ker
   f32x16 oacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) oacc[t] = (f32x16){};
-  float m_ref = -INFINITY;   // running row max, log2 units
+  float m_ref = -INFINITY;   // reference row max, log2 units
   float l_part = 0.f;        // this half-wave's share of sum 2^8 p
   const float c = a.c;
 
@@ -217,7 +222,9 @@ __global__ __launch_bounds__(64 * kF8Waves, (D == 128 ? 3 : 4)) void fwd_fp8_ker
         s[t] = mfma_fp8(lds_read32(kb, (kl ^ (uint32_t)(ks << 6)) + (uint32_t)(16 * t * D)), qf[ks], s[t]);
   };
 
-  // Softmax of one step against the exact running max, and P as e4m3 codes.
+  // Softmax of one step against a reference max at most kF8Slack below the
+  // running max (moved to the exact running max when it falls further
+  // behind), and P as e4m3 codes.
   auto softmax = [&](auto mask_tag, f32x16 (&s)[2], int k0, i32x8& pf) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if constexpr (MASK) {
@@ -237,7 +244,7 @@ __global__ __launch_bounds__(64 * kF8Waves, (D == 128 ? 3 : 4)) void fwd_fp8_ker
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
     mx = max_halves(mx);
     const float mcand = (mx == -INFINITY) ? -INFINITY : mx * c;
-    if (__any(mcand > m_ref)) {
+    if (__any(mcand > m_ref + kF8Slack)) {
       const float m_new = fmaxf(m_ref, mcand);
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
       l_part *= alpha;
