@@ -91,6 +91,24 @@ def check_lse(got, ref, what):
     return float(err.max())
 
 
+def check_dropout(got, ref, s, what):
+    """Bar for outputs of the dropout entry points, s = the scale of kept
+    probabilities: every kept term is multiplied by s, so outputs grow by up to
+    s and so does the bf16 rounding of them (half an ulp is up to 2^-9 |x|).
+    An element may differ from the oracle by 2^-8 |ref| (the rounding of the
+    result, with margin) plus s times the plain path's absolute bar (2e-2);
+    the mean error may reach s times the plain mean bar plus 2^-8 times the
+    mean |ref|.  A wrong mask element moves a result by a whole term."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    err = np.abs(got - ref)
+    over = err - 2.0 ** -8 * np.abs(ref)
+    assert over.max() <= BF16_MAX * s, f"{what}: max abs err {err.max():.3e} ({over.max():.3e} beyond 2^-8 |ref|)"
+    mean_bar = BF16_MEAN * s + 2.0 ** -8 * np.abs(ref).mean()
+    assert err.mean() <= mean_bar, f"{what}: mean abs err {err.mean():.3e} > {mean_bar:.2e}"
+
+
 def inputs(shape, dtype, seed, with_do=False, qk_mult=1.0):
     host = synth.make_inputs(shape, dtype, seed, with_do=with_do, qk_mult=qk_mult)
     dev = {k: to_dev(v) for k, v in host.items()}
