@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP8_TFLOPS = 5033.2      # 256 CU x 2.4 GHz x 8192 dense e4m3 FLOP/clk/CU
+PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention TFLOP/s (bf16 fwd & fwd+bwd, causal) and % of MI355X MFMA peak"
 
@@ -213,6 +214,39 @@ def time_forward_fp8(fa, torch, B, N, H, d, seed, iters, causal=True, qk_mult=1.
     return {"shape_BNHd": [B, N, H, d], "causal": causal, "median_ms": round(med, 4),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}}
+
+
+def time_fp32(fa, torch, B, N, H, d, causal, iters):
+    """fa_forward_f32 and fa_backward_f32 (fp32 tensors, fp32 matrix cores):
+    median times, and rates against the fp32 matrix peak (the backward at the
+    credited 2.5x forward FLOPs)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    q, k, v, do = (torch.randn((B, N, H, d), generator=g, device="cuda", dtype=torch.float32) for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device="cuda")
+    scale = d ** -0.5
+    calls = {"fwd": lambda: fa.fa_forward(q, k, v, o, lse, scale, causal),
+             "bwd": lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, ws, scale, causal)}
+    out = {"shape_BNHd": [B, N, H, d], "causal": causal}
+    st = torch.cuda.current_stream()
+    for name, call in calls.items():
+        warm_up(call, torch)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        ev[0].record(st)
+        for i in range(iters):
+            call()
+            ev[i + 1].record(st)
+        torch.cuda.synchronize()
+        ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+        med = ms[len(ms) // 2]
+        tf = (1.0 if name == "fwd" else 2.5) * fwd_flops(B, H, N, d, causal) / (med * 1e-3) / 1e12
+        out[name] = {"median_ms": round(med, 4), "tflops": round(tf, 2),
+                     "pct_of_fp32_matrix_peak": round(100 * tf / PEAK_FP32_MATRIX_TFLOPS, 1)}
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    return out
 
 
 def time_dropout(fa, torch, B, N, H, d, p, iters):
@@ -549,6 +583,12 @@ def main():
             "c3_noncausal": time_forward_fp8(fa, torch, 4, 4096, 16, 128, 3, 20, causal=False),
             "c4": time_forward_fp8(fa, torch, 1, 32768, 32, 128, 4, 10, qk_mult=2.0),
         }
+        log("bench: fp32 path (fp32 matrix cores)")
+        result["fp32"] = {
+            "c1": time_fp32(fa, torch, 1, 256, 1, 64, False, 50),
+            "large": time_fp32(fa, torch, 1, 4096, 16, 128, False, 10),
+        }
+        result["fp32"]["c1"]["note"] = "config 1: correctness case, latency-bound (4 workgroups)"
         log("bench: forward + backward with dropout")
         result["dropout"] = time_dropout(fa, torch, 2, 8192, 16, 64, 0.1, 10)
         log("bench: single-pass backward (atomic dQ) beside the two-pass backward")
