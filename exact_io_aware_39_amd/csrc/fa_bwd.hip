@@ -620,13 +620,14 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 // Waves per SIMD the dK/dV and fused kernels are compiled for (measured on
 // MI355X).  d = 64: 3 (168 registers; without the mask five dwords spill,
 // still 3% faster than 2; dropout without the mask keeps 2, where 3 would
-// spill 48).  d = 128 causal: 2 (256 registers, faster than 1); d = 128 without
-// mask: 1 (the dQ tile needs about 280 registers; at 2 the fused kernel
-// spills some 60).  d = 256: 1 (the dK and dV accumulators of a wave alone
-// take 256 registers; a few more spill without the mask).
+// spill 48).  d = 128: 2 (256 registers; without the mask the fused kernel's
+// dQ tile, which the compiler would give about 280, spills 57 dwords, and
+// is still 1.44x faster than at one wave per SIMD).  d = 256: 1 (the dK and
+// dV accumulators of a wave alone take 256 registers; a few more spill
+// without the mask).
 template <int D, bool CAUSAL, bool DROP>
 constexpr int bwd_min_waves() {
-  return D == 64 ? (CAUSAL || !DROP ? 3 : 2) : D == 128 ? (CAUSAL ? 2 : 1) : 1;
+  return D == 64 ? (CAUSAL || !DROP ? 3 : 2) : D == 128 ? 2 : 1;
 }
 
 template <int D, bool CAUSAL, bool DROP>
@@ -665,7 +666,7 @@ __global__ __launch_bounds__(256) void dq_from_acc_kernel(const f32x4* __restric
 }
 
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (D == 128 ? 2 : 3)) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[dq_lds_bytes<D>()];
   int bh, qt;
   tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, true, bh, qt);
