@@ -72,10 +72,16 @@ constexpr int fwd_mode() { return D == 128 && !DROP ? 3 : 0; }
 // rows, half the copy instructions per row; 3% faster on MI355X than 4); with
 // the mask the waves of a 256-row tile that finish their diagonal early
 // would idle through the rest (3% slower), so it keeps 4.
+// At D = 256 without dropout an 8-wave form (two waves per SIMD over the same
+// 128 KB of K and V buffers, 37 dwords spilled) is chosen at run time for
+// grids of at least kWide256Grid of its workgroups: 4-7% faster on MI355X
+// there, and up to 37% slower on small grids, which have half as many
+// workgroups as with 4 waves.
 template <int D, bool CAUSAL, bool DROP = false>
 constexpr int fwd_wg_waves() { return fwd_mode<D, CAUSAL, DROP>() == 3 || (D == 64 && !CAUSAL && !DROP) ? 8 : 4; }
-template <int D, bool DROP>
-constexpr int fwd_waves() { return D == 64 ? (DROP ? 3 : 4) : D == 128 ? 2 : 1; }
+template <int D, bool DROP, int W = 4>
+constexpr int fwd_waves() { return D == 64 ? (DROP ? 3 : 4) : D == 128 ? 2 : (W == 8 ? 2 : 1); }
+constexpr int kWide256Grid = 512;
 
 // Buffer index carried by a step's buffer tag: the constant of a
 // compile-time tag, 0 for a run-time one (whose offset is in the pointer).
@@ -98,15 +104,16 @@ struct FwdArgs {
   DropParams drop;   // used by the DROP instantiations only
 };
 
-template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), (fwd_waves<D, DROP>())) void fwd_bf16_kernel(FwdArgs a) {
+template <int D, bool CAUSAL, bool DROP, int WGW = fwd_wg_waves<D, CAUSAL, DROP>()>
+__global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int KS = D / 16;           // k-steps of the score product
   constexpr int DT = D / 32;           // 32-wide output tiles
   constexpr int RB = D * 2;            // bytes per LDS row (dense, chunks swizzled)
   constexpr int TILE = kBc * RB;       // bytes of one K or V tile
   constexpr int MODE = fwd_mode<D, CAUSAL, DROP>();
-  constexpr int kWaves = fwd_wg_waves<D, CAUSAL, DROP>();
+  constexpr int kWaves = WGW;
+  static_assert(MODE == 0 || kWaves == 8, "the ping-pong loop takes 8 waves");
   constexpr int kBr = 32 * kWaves;     // query rows per workgroup
   constexpr int CPW = TILE / 1024 / kWaves;   // 1 KB global->LDS copies per wave per tile
   // Mode 0 keeps a ring of NB tiles: copies run NB - 1 tiles ahead.  Two
@@ -635,12 +642,11 @@ __global__ __launch_bounds__((64 * fwd_wg_waves<D, CAUSAL, DROP>()), (fwd_waves<
   }
 }
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool DROP, int W = fwd_wg_waves<D, CAUSAL, DROP>()>
 hipError_t launch(FwdArgs args, int BH, hipStream_t stream) {
-  constexpr int W = fwd_wg_waves<D, CAUSAL, DROP>();
   args.nqt = (args.N + 32 * W - 1) / (32 * W);
   const int grid = args.nqt * BH;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP>), dim3(grid), dim3(64 * W), 0, stream, args);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, W>), dim3(grid), dim3(64 * W), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -648,7 +654,13 @@ template <bool DROP>
 hipError_t launch_any(const FwdArgs& a, const AttnShape& s, hipStream_t stream) {
   const int BH = s.B * s.H;
   if (s.d == 64) return s.causal ? launch<64, true, DROP>(a, BH, stream) : launch<64, false, DROP>(a, BH, stream);
-  if (s.d == 256) return s.causal ? launch<256, true, DROP>(a, BH, stream) : launch<256, false, DROP>(a, BH, stream);
+  if (s.d == 256) {
+    if constexpr (!DROP) {
+      if ((int64_t)((s.N + 255) / 256) * BH >= kWide256Grid)
+        return s.causal ? launch<256, true, false, 8>(a, BH, stream) : launch<256, false, false, 8>(a, BH, stream);
+    }
+    return s.causal ? launch<256, true, DROP>(a, BH, stream) : launch<256, false, DROP>(a, BH, stream);
+  }
   return s.causal ? launch<128, true, DROP>(a, BH, stream) : launch<128, false, DROP>(a, BH, stream);
 }
 

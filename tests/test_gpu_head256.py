@@ -43,6 +43,34 @@ def test_midsize(causal):
     run_backward((1, 2048, 4, D), "bf16", 6301, causal, D ** -0.5, heads=[(0, 1), (0, 2)], tag="d256 mid")
 
 
+@pytest.mark.parametrize("shape", [(2, 4096, 16, D), (1, 4000, 32, D)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_wide_grid(shape, causal):
+    """Grids of at least 512 workgroups of 256 rows take the 8-wave form of the
+    d = 256 forward (ragged last tile in the second shape)."""
+    require_gpu()
+    B, N, H, _ = shape
+    run_forward(shape, "bf16", 6500 + N, causal, D ** -0.5, heads=[(0, 0), (B - 1, H - 1)], tag="d256 wide")
+
+
+def test_cross_forward_wide_grid():
+    """Nq rows against Nk keys with 512 workgroups of 256 rows: the 8-wave form
+    with a query offset under the mask."""
+    require_gpu()
+    B, Nq, Nk, H = 1, 2000, 3000, 64
+    say("d256 wide cross", B, Nq, Nk, H)
+    host = synth.make_decode_inputs(B, Nq, Nk, H, D, seed=6600)
+    q, k, v = (to_dev(host[x]) for x in "qkv")
+    f64 = {x: synth.decode(host[x]) for x in "qkv"}
+    scale = synth.f32(D ** -0.5)
+    o, lse = fa.forward_cross(q, k, v, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    for h in (0, H - 1):
+        o_ref, lse_ref = ora.decode(f64["q"][0, :, h], f64["k"][0, :, h], f64["v"][0, :, h], scale, True)
+        check(to64(o[0, :, h]), o_ref, "bf16", f"d256 wide cross O h={h}")
+        check_lse(to64(lse[0, h]), lse_ref, f"d256 wide cross LSE h={h}")
+
+
 @pytest.mark.parametrize("B,Nq,Nk,H,causal", [(1, 100, 300, 2, True), (1, 257, 1000, 2, False),
                                              (2, 64, 65, 1, True)])
 def test_cross_forward_and_backward(B, Nq, Nk, H, causal):

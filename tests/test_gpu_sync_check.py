@@ -70,6 +70,7 @@ SHAPES = [
     (1, 1100, 8, 128),
     (1, 200, 2, 256),
     (1, 600, 2, 256),
+    (2, 4096, 16, 256),   # the 8-wave form of the d = 256 forward (512 workgroups)
 ]
 
 
