@@ -270,13 +270,24 @@ __global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_b
   //  the exact running max when it grows by more than 2^8.
   //  Other steps exponentiate against the current reference straight away and
   //  only look at the row max (and redo the step) if some row's share of the
-  //  sum exceeds 2^16, which bounds every probability by 2^16; the reference
-  //  is -inf before the first step, so the first step always takes that path.
+  //  sum exceeds 2^16, which bounds every probability by 2^16.
+  //  The first step of a wave, when no key of it is hidden (mask_tag of
+  //  value 2), sets the reference to the row max before exponentiating: the
+  //  reference is -inf before it, so exponentiating first would always redo
+  //  the step, and nothing has been accumulated yet to rescale.
   //  A move of the reference rescales the output accumulated so far.
   auto softmax_tile = [&](auto mask_tag, f32x16 (&s)[2], int k0, bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int MT = (int)decltype(mask_tag)::value;
     float lsum;
-    if constexpr (MASK) {
+    if constexpr (MT == 2) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+      m_ref = max_halves(mx) * c;
+      lsum = exp_tile(std::false_type{}, s, pb, k0);
+    } else if constexpr (MT == 1) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -483,11 +494,13 @@ __global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_b
         static_assert(PK < 4 || PK == 7, "product kind");
       }
     };
-    // Softmax of tile t: SK = 0 none, 1 every key visible, 2 masked.
+    // Softmax of tile t: SK = 0 none, 1 every key visible, 2 masked, 4 the
+    // wave's first step with every key visible.
     auto softmax = [&](int t, auto sk_tag) __attribute__((always_inline)) {
       constexpr int SK = decltype(sk_tag)::value;
       if constexpr (SK == 1) softmax_tile(std::false_type{}, sc, t * kBc, pb);
       if constexpr (SK == 2) softmax_tile(std::true_type{}, sc, t * kBc, pb);
+      if constexpr (SK == 4) softmax_tile(std::integral_constant<int, 2>{}, sc, t * kBc, pb);
     };
     // One step: the products of step t, then the softmax of tile t, each
     // ending with its phase barrier.
@@ -506,6 +519,7 @@ __global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_b
     using P1 = std::integral_constant<int, 1>;
     using P2 = std::integral_constant<int, 2>;
     using P3 = std::integral_constant<int, 3>;
+    using P4 = std::integral_constant<int, 4>;
     using P7 = std::integral_constant<int, 7>;
     // Leading tiles every key of which this wave's rows see.
     const int nfree = __builtin_amdgcn_readfirstlane(
@@ -521,7 +535,7 @@ __global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_b
       copies(0);
       phase_end();
     }
-    if (nfree > 0) step(0, P1{}, P1{});
+    if (nfree > 0) step(0, P1{}, P4{});
     else step(0, P1{}, P2{});
     int t = 1;
     for (; t < nfree; ++t) step(t, P3{}, P1{});
@@ -593,20 +607,33 @@ __global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_b
     using B2 = std::integral_constant<int, 2>;
     // Unmasked steps kt .. end - 1 from kt = 0, NB per iteration.
     auto run_free = [&](int& kt, int end) __attribute__((always_inline)) {
+      using First = std::integral_constant<int, 2>;
       if constexpr (NB == 3) {
-        for (; kt + 2 < end; kt += 3) {
-          step(kt, std::false_type{}, B0{});
-          step(kt + 1, std::false_type{}, B1{});
-          step(kt + 2, std::false_type{}, B2{});
-        }
-        if (kt < end) step(kt++, std::false_type{}, B0{});
+        if (kt < end) step(kt++, First{}, B0{});
         if (kt < end) step(kt++, std::false_type{}, B1{});
-      } else {
+        for (; kt + 2 < end; kt += 3) {
+          step(kt, std::false_type{}, B2{});
+          step(kt + 1, std::false_type{}, B0{});
+          step(kt + 2, std::false_type{}, B1{});
+        }
+        if (kt < end) step(kt++, std::false_type{}, B2{});
+        if (kt < end) step(kt++, std::false_type{}, B0{});
+      } else if constexpr (D == 64) {
+        // the loop keeps buffer 0 first (measured faster at this width)
+        if (kt < end) step(kt++, First{}, B0{});
+        if (kt < end) step(kt++, std::false_type{}, B1{});
         for (; kt + 1 < end; kt += 2) {
           step(kt, std::false_type{}, B0{});
           step(kt + 1, std::false_type{}, B1{});
         }
         if (kt < end) step(kt++, std::false_type{}, B0{});
+      } else {
+        if (kt < end) step(kt++, First{}, B0{});
+        for (; kt + 1 < end; kt += 2) {
+          step(kt, std::false_type{}, B1{});
+          step(kt + 1, std::false_type{}, B0{});
+        }
+        if (kt < end) step(kt++, std::false_type{}, B1{});
       }
     };
     int kt = 0;
