@@ -14,7 +14,9 @@ that.  `roofline` covers the kernel with the largest average duration,
 timed with HIP events recorded around each launch on the stream the kernels
 run on.  `cpu_baseline` times the fp64 CPU oracle on one head of the same
 workload.  `forward_only` times the forward alone on the two long causal
-workloads ([4, 4096, 16, 128] and [1, 32768, 32, 128] with Q, K doubled).
+workloads ([4, 4096, 16, 128] and [1, 32768, 32, 128] with Q, K doubled);
+`head256` times fa_forward and fa_backward at head size 256 ([2, 4096, 16,
+256], causal and not).
 
     python bench.py --copy-calibration
 
@@ -245,6 +247,41 @@ def time_fp32(fa, torch, B, N, H, d, causal, iters):
         tf = (1.0 if name == "fwd" else 2.5) * fwd_flops(B, H, N, d, causal) / (med * 1e-3) / 1e12
         out[name] = {"median_ms": round(med, 4), "tflops": round(tf, 2),
                      "pct_of_fp32_matrix_peak": round(100 * tf / PEAK_FP32_MATRIX_TFLOPS, 1)}
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    return out
+
+
+def time_fwd_bwd(fa, torch, B, N, H, d, causal, iters):
+    """fa_forward and fa_backward (preprocess + both passes) timed apart:
+    medians and the rates at 4 B H N^2 d (halved under the mask) and 2.5x
+    that."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(10)
+    q, k, v, do = (torch.randn((B, N, H, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device="cuda")
+    scale = d ** -0.5
+    calls = {"fwd": lambda: fa.fa_forward(q, k, v, o, lse, scale, causal),
+             "bwd": lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, ws, scale, causal)}
+    out = {"shape_BNHd": [B, N, H, d], "causal": causal}
+    st = torch.cuda.current_stream()
+    for name, fn in calls.items():
+        warm_up(fn, torch)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        ev[0].record(st)
+        for i in range(iters):
+            fn()
+            ev[i + 1].record(st)
+        torch.cuda.synchronize()
+        ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+        med = ms[len(ms) // 2]
+        tf = (1.0 if name == "fwd" else 2.5) * fwd_flops(B, H, N, d, causal) / (med * 1e-3) / 1e12
+        out[name] = {"median_ms": round(med, 4), "p10_ms": round(pct(ms, 0.1), 4), "p90_ms": round(pct(ms, 0.9), 4),
+                     ("tflops" if name == "fwd" else "tflops_credited"): round(tf, 1),
+                     "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
     del q, k, v, do, o, lse, dq, dk, dv, ws
     return out
 
@@ -577,6 +614,11 @@ def main():
             "c4": time_forward_only(fa, torch, 1, 32768, 32, 128, synth.f32(128 ** -0.5), 2.0, 4, 10),
         }
         result["forward_only"]["c2"]["note"] = "reported, not targeted (64 workgroups for 256 CUs)"
+        log("bench: head size 256")
+        result["head256"] = {
+            "causal": time_fwd_bwd(fa, torch, 2, 4096, 16, 256, True, 20),
+            "noncausal": time_fwd_bwd(fa, torch, 2, 4096, 16, 256, False, 10),
+        }
         log("bench: FP8 (e4m3) forward")
         result["forward_fp8"] = {
             "c3_causal": time_forward_fp8(fa, torch, 4, 4096, 16, 128, 3, 20),

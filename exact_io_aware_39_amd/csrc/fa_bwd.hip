@@ -27,6 +27,10 @@
 //                 one scalar per lane, and dS^T feeds dQ^T += K^T dS^T directly.
 // fa_backward runs 2 and 3 as one grid (bwd_fused) ordered heaviest first, so
 // the two passes share one tail; the split entry points launch them apart.
+// At head size 256 (without dropout) the separate passes, and the fused grid
+// under the causal mask, run column-split forms of both tiles: eight waves,
+// each pair holding the same rows and half of the columns, whose partial
+// scores meet in LDS (two waves per SIMD instead of one).
 // Both passes stage their streamed tiles with buffer -> LDS copies into two
 // LDS slots.  At head size 64 these plain loops at three waves per SIMD
 // measured faster than software-pipelined forms (the score products of the
@@ -131,14 +135,15 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* tile, uint32_t base, int t
 }
 
 // Per-lane byte offsets of the buffer -> LDS copies of a tile of ROWS rows:
-// copy i of a wave fills LDS block (wave + 4 i); lane l holds physical chunk
-// slot%CH of row slot/CH, i.e. logical chunk (slot%CH) ^ swz(row).
-template <int D, int CPW>
+// copy i of a wave fills LDS block (wave + NW i) (NW waves in the
+// workgroup); lane l holds physical chunk slot%CH of row slot/CH, i.e.
+// logical chunk (slot%CH) ^ swz(row).
+template <int D, int CPW, int NW = 4>
 __device__ __forceinline__ void stage_offsets(uint32_t (&voff)[CPW], int wave, int lane, int64_t rs) {
   constexpr int CH = D / 8;
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
-    const int slot = (wave + 4 * i) * 64 + lane;
+    const int slot = (wave + NW * i) * 64 + lane;
     const int row = slot / CH;
     voff[i] = (uint32_t)(row * rs * 2) + (uint32_t)(((slot % CH) ^ swz<D>(row)) * 16);
   }
@@ -462,6 +467,221 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
   }
 }
 
+// ------------------------------------------------------------------ d = 256: columns split over wave pairs
+// At d = 256 the dK and dV accumulators of 32 keys alone take 256 registers
+// of a wave, which leaves one wave per SIMD and nothing to hide one wave's
+// latencies.  Here eight waves share the 128-key tile: waves w and w + 4
+// hold the same 32 keys, wave w columns 0 .. 127 and wave w + 4 columns
+// 128 .. 255 of K, V, dK and dV (two waves per SIMD).  Each forms its
+// columns' part of S = Q K^T and dP = dO V^T, the two parts meet in LDS as
+// fp32, and both waves go on from the same sums (a + b and b + a are the
+// same fp32 value); each then updates its own columns of dV and dK.
+constexpr int kSplitWaves = 8;
+constexpr int kXchgBytes = kSplitWaves * 64 * 32 * 4;   // 32 floats per lane and wave
+
+template <int D>
+constexpr int dkdv_split_lds_bytes() { return 2 * (2 * 32 * D * 2 + 512) + kXchgBytes; }
+
+// Barrier once this wave's LDS stores have completed.  Global -> LDS copies
+// still in flight are not waited for (__syncthreads would drain them).
+__device__ __forceinline__ void lds_store_barrier() {
+  sync_check_drain();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// This wave's partial S and dP go to its exchange slot (lane-major float4s:
+// slot row r4 of lane l at float4 index 64 r4 + l, rows 0-3 S, 4-7 dP).
+__device__ __forceinline__ void xchg_put(f32x4* slot, int lane, const f32x16& s, const f32x16& p) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    slot[64 * r4 + lane] = (f32x4){s[4 * r4], s[4 * r4 + 1], s[4 * r4 + 2], s[4 * r4 + 3]};
+    slot[64 * (4 + r4) + lane] = (f32x4){p[4 * r4], p[4 * r4 + 1], p[4 * r4 + 2], p[4 * r4 + 3]};
+  }
+}
+// Adds the partner's partial S and dP from its exchange slot.
+__device__ __forceinline__ void xchg_add(const f32x4* slot, int lane, f32x16& s, f32x16& p) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const f32x4 os = slot[64 * r4 + lane], op = slot[64 * (4 + r4) + lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[4 * r4 + e] += os[e];
+      p[4 * r4 + e] += op[e];
+    }
+  }
+}
+
+// dK, dV of key tile kt of head bh with the columns split over wave pairs
+// (eight waves, 32 query rows per step).
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dkdv_tile_split(const BwdArgs& a, int bh, int kt, char* smem) {
+  constexpr int DH = D / 2;                 // columns per wave
+  constexpr int KS = DH / 16, DT = DH / 32, RB = D * 2;
+  constexpr int kBq = 32;
+  constexpr int TILE = kBq * RB;            // one Q or dO tile
+  constexpr int CPW = TILE / 1024 / kSplitWaves;
+  constexpr int SLOT = 2 * TILE + 512;      // Q, dO, then 64 floats of -LSE log2 e and of -D
+  static_assert(CPW * kSplitWaves * 1024 == TILE, "the copies cover the tile");
+  static_assert(2 * SLOT + kXchgBytes == dkdv_split_lds_bytes<D>(), "LDS layout");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int kg = wave & 3;                                       // key group
+  const int dh = __builtin_amdgcn_readfirstlane(wave >> 2);     // column half
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int N = a.N, Nk = a.Nk, qoff = a.qoff;
+  const int64_t rs = (int64_t)a.H * D;
+  const int64_t base = ((int64_t)b * N * a.H + h) * D;      // Q, dO
+  const int64_t kbase = ((int64_t)b * Nk * a.H + h) * D;    // K, V, dK, dV
+  const float* dstat = a.ws + (int64_t)bh * N;
+  const float* nlstat = a.ws + a.bhn + (int64_t)bh * N;
+  f32x4* const xmine = reinterpret_cast<f32x4*>(smem + 2 * SLOT) + wave * 8 * 64;
+  const f32x4* const xpeer = reinterpret_cast<const f32x4*>(smem + 2 * SLOT) + (wave ^ 4) * 8 * 64;
+
+  const int k0 = kt * kKeysPerWg;
+  const int kw0 = k0 + 32 * kg;
+  const int mykey = kw0 + l32;
+
+  // K^T and V^T as B operands: this lane's key, chunk 2 ks + hh of the half.
+  bf16x8 kf[KS], vf[KS];
+  {
+    const int64_t kr = kbase + (int64_t)min(mykey, Nk - 1) * rs + dh * DH;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = *reinterpret_cast<const bf16x8*>(a.k + kr + (2 * ks + hh) * 8);
+      vf[ks] = *reinterpret_cast<const bf16x8*>(a.v + kr + (2 * ks + hh) * 8);
+    }
+  }
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) { dk[t] = (f32x16){}; dv[t] = (f32x16){}; }
+
+  const int qstart = CAUSAL ? max(0, k0 - qoff) : 0;
+  const int nsteps = (N - qstart + kBq - 1) / kBq;
+
+  uint32_t voff[CPW];
+  stage_offsets<D, CPW, kSplitWaves>(voff, wave, lane, rs);
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  auto stage = [&](int s, char* slot) {
+    const int qi0 = qstart + s * kBq;
+    const int rows = min(N - qi0, kBq);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + base + (int64_t)qi0 * rs, (uint32_t)(rows * rs * 2));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.dout + base + (int64_t)qi0 * rs, (uint32_t)(rows * rs * 2));
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      buffer_to_lds16(rq, voff[i], slot + (wu + kSplitWaves * i) * 1024);
+      buffer_to_lds16(rg, voff[i], slot + TILE + (wu + kSplitWaves * i) * 1024);
+    }
+    if (wu == 0)
+      buffer_to_lds4(make_rsrc(nlstat + qi0, (uint32_t)(rows * 4)), lane * 4, slot + 2 * TILE);
+    else if (wu == 1)
+      buffer_to_lds4(make_rsrc(dstat + qi0, (uint32_t)(rows * 4)), lane * 4, slot + 2 * TILE + 256);
+  };
+
+  // Fragment bases moved to this wave's columns: byte bit 8 of both bases is
+  // zero (the chunk swizzle stays below chunk 16), so + 256 dh selects logical
+  // chunks 16 dh .. 16 dh + 15 under every XOR the reads apply.
+  const uint32_t rfb = row_frag_base<D>(lane) + (uint32_t)(dh * DH * 2);
+  const uint32_t tfb = tr_frag_base<D>(lane) + (uint32_t)(dh * DH * 2);
+  // This half's part of S = Q K^T and dP = dO V^T (lane = key, register r =
+  // query row 8(r/4) + 4hh + r%4); half 0's dP starts from -D of each row, so
+  // the sum of the halves is dP - D.
+  auto scores = [&](const char* slot, f32x16& sacc, f32x16& pacc) __attribute__((always_inline)) {
+    sacc = (f32x16){};
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 nd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (8 * g4 + 4 * hh) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pacc[4 * g4 + e] = dh == 0 ? nd[e] : 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      sacc = mfma32x32x16(lds_read_b128(slot, rfb ^ (ks << 5)), kf[ks], sacc);
+      pacc = mfma32x32x16(lds_read_b128(slot + TILE, rfb ^ (ks << 5)), vf[ks], pacc);
+    }
+  };
+  const float c = a.c;
+  // P, dS of the step's rows (qi0 ..) and this half's dV, dK updates.
+  auto update = [&](auto mask_tag, const char* slot, const f32x16& sacc, const f32x16& pacc, int qi0)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float p[8], ds[8];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int g4 = 2 * u + g;
+        const f32x4 nl = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + (8 * g4 + 4 * hh) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float pv = fast_exp2(__builtin_fmaf(sacc[r], c, nl[e]));
+          if constexpr (MASK) {
+            const int qrow = qi0 + 8 * g4 + 4 * hh + e;
+            const bool hide = qrow >= N || (CAUSAL && mykey > qrow + qoff);
+            pv = hide ? 0.f : pv;
+          }
+          p[4 * g + e] = pv;
+          ds[4 * g + e] = pv * pacc[r];
+        }
+      }
+      const bf16x8 pb = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      const bf16x8 db = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        dv[t] = mfma32x32x16(tr_frag<D>(slot + TILE, tfb, t, 0, u), pb, dv[t]);
+        dk[t] = mfma32x32x16(tr_frag<D>(slot, tfb, t, 0, u), db, dk[t]);
+      }
+    }
+  };
+  // One step (MODE 1 unmasked, 2 masked, 0 no row sees this pair's keys):
+  // publish query tile s and copy tile s + 1, the partial products, the
+  // exchange, then P, dS and the updates.  Every wave passes both barriers of
+  // every step, whatever its mode.  The exchange slots are rewritten only
+  // after the next step's first barrier, which the partner passes once it
+  // has read them.
+  auto step = [&](int s, auto mode_tag) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    char* slot = smem + (s & 1) * SLOT;
+    wait_vmem();
+    block_sync();
+    if (s + 1 < nsteps) stage(s + 1, smem + ((s + 1) & 1) * SLOT);
+    f32x16 sacc, pacc;
+    if constexpr (MODE != 0) {
+      scores(slot, sacc, pacc);
+      xchg_put(xmine, lane, sacc, pacc);
+    }
+    lds_store_barrier();
+    if constexpr (MODE != 0) {
+      xchg_add(xpeer, lane, sacc, pacc);
+      update(std::bool_constant<MODE == 2>{}, slot, sacc, pacc, qstart + s * kBq);
+    }
+  };
+  // Sections with one update path each, as in dkdv_tile.
+  const int nfull = (N - qstart) / kBq;
+  int s_vis = 0, s_unm = 0;
+  if constexpr (CAUSAL) {
+    s_vis = min(nsteps, max(0, ceil_div(kw0 - qoff - (kBq - 1) - qstart, kBq)));
+    s_unm = min(nsteps, max(s_vis, ceil_div(kw0 + 31 - qoff - qstart, kBq)));
+    s_vis = __builtin_amdgcn_readfirstlane(s_vis);
+    s_unm = __builtin_amdgcn_readfirstlane(s_unm);
+  }
+  using M0 = std::integral_constant<int, 0>;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
+  stage(0, smem);
+  int s = 0;
+  for (; s < s_vis; ++s) step(s, M0{});
+  for (; s < s_unm; ++s) step(s, M2{});
+  for (; s < nfull; ++s) step(s, M1{});
+  for (; s < nsteps; ++s) step(s, M2{});
+
+  if (mykey < Nk) {
+    store_row_frags<DH>(a.dk + kbase + (int64_t)mykey * rs + dh * DH, dk, hh, a.scale);
+    store_row_frags<DH>(a.dv + kbase + (int64_t)mykey * rs + dh * DH, dv, hh, 1.f);
+  }
+}
+
 // ------------------------------------------------------------------ dQ pass
 constexpr int kQPerWg = 128;   // 4 waves x 32 queries
 constexpr int kBk = 64;        // keys per step
@@ -616,6 +836,159 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
   if (myq < N) store_row_frags<D>(a.dq + base + (int64_t)myq * rs, dq, hh, a.scale);
 }
 
+// dQ of query tile qtile of head bh with the columns split over wave pairs
+// (eight waves; waves w and w + 4 hold the same 32 queries, wave w columns
+// 0 .. D/2 - 1 of Q, dO and dQ, wave w + 4 the rest).  K and V go through LDS
+// 32 keys per step (two 32 KB K/V slot pairs beside the 64 KB exchange).
+constexpr int kBkSplit = 32;
+
+template <int D>
+constexpr int dq_split_lds_bytes() { return 2 * 2 * kBkSplit * D * 2 + kXchgBytes; }
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dq_tile_split(const BwdArgs& a, int bh, int qtile, char* smem) {
+  constexpr int DH = D / 2;
+  constexpr int KS = DH / 16, DT = DH / 32, RB = D * 2;
+  constexpr int TILE = kBkSplit * RB;
+  constexpr int CPW = TILE / 1024 / kSplitWaves;
+  static_assert(CPW * kSplitWaves * 1024 == TILE, "the copies cover the tile");
+  static_assert(4 * TILE + kXchgBytes == dq_split_lds_bytes<D>(), "LDS layout");
+  char* const kbuf = smem;                 // slots 0, 1
+  char* const vbuf = smem + 2 * TILE;      // slots 0, 1
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int qg = wave & 3;                                       // query group
+  const int dh = __builtin_amdgcn_readfirstlane(wave >> 2);     // column half
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int N = a.N, Nk = a.Nk, qoff = a.qoff;
+  const int64_t rs = (int64_t)a.H * D;
+  const int64_t base = ((int64_t)b * N * a.H + h) * D;      // Q, dO, dQ
+  const int64_t kbase = ((int64_t)b * Nk * a.H + h) * D;    // K, V
+  f32x4* const xmine = reinterpret_cast<f32x4*>(smem + 4 * TILE) + wave * 8 * 64;
+  const f32x4* const xpeer = reinterpret_cast<const f32x4*>(smem + 4 * TILE) + (wave ^ 4) * 8 * 64;
+
+  const int q0 = qtile * kQPerWg;
+  const int qw0 = q0 + 32 * qg;
+  const int myq = qw0 + l32;
+  const int qc = min(myq, N - 1);
+
+  bf16x8 qf[KS], gf[KS];
+  {
+    const int64_t qr = base + (int64_t)qc * rs + dh * DH;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qr + (2 * ks + hh) * 8);
+      gf[ks] = *reinterpret_cast<const bf16x8*>(a.dout + qr + (2 * ks + hh) * 8);
+    }
+  }
+  const float nl2 = a.ws[a.bhn + (int64_t)bh * N + qc];
+  const float ndval = a.ws[(int64_t)bh * N + qc];   // -D of this lane's query
+  const float nd_half = dh == 0 ? ndval : 0.f;       // half 0 carries it
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) dq[t] = (f32x16){};
+
+  const int kend = CAUSAL ? min(Nk, q0 + qoff + kQPerWg) : Nk;
+  const int nkt = (kend + kBkSplit - 1) / kBkSplit;
+
+  uint32_t voff[CPW];
+  stage_offsets<D, CPW, kSplitWaves>(voff, wave, lane, rs);
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  auto stage_rows = [&](const __bf16* src, int t, char* dst) {
+    const int rows = min(Nk - t * kBkSplit, kBkSplit);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        make_rsrc(src + kbase + (int64_t)t * kBkSplit * rs, (uint32_t)(rows * rs * 2));
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, voff[i], dst + (wu + kSplitWaves * i) * 1024);
+  };
+
+  // Bases moved to this wave's columns (see dkdv_tile_split).
+  const uint32_t rfb = row_frag_base<D>(lane) + (uint32_t)(dh * DH * 2);
+  const uint32_t tfb = tr_frag_base<D>(lane) + (uint32_t)(dh * DH * 2);
+  // This half's part of S^T = K Q^T and dP^T = V dO^T (lane = query,
+  // register r = key 8(r/4) + 4hh + r%4 of the step); half 0's dP^T starts
+  // from -D, so the sum of the halves is dP^T - D.
+  auto scores = [&](const char* kt, const char* vt, f32x16& sacc, f32x16& pacc) __attribute__((always_inline)) {
+    sacc = (f32x16){};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pacc[r] = nd_half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      sacc = mfma32x32x16(lds_read_b128(kt, rfb ^ (ks << 5)), qf[ks], sacc);
+      pacc = mfma32x32x16(lds_read_b128(vt, rfb ^ (ks << 5)), gf[ks], pacc);
+    }
+  };
+  const float c = a.c;
+  auto update = [&](auto mask_tag, const char* kt, const f32x16& sacc, const f32x16& pacc, int k0)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float ds[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * u + e;
+        float pv = fast_exp2(__builtin_fmaf(sacc[r], c, nl2));
+        if constexpr (MASK) {
+          const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool hide = key >= Nk || (CAUSAL && key > myq + qoff);
+          pv = hide ? 0.f : pv;
+        }
+        ds[e] = pv * pacc[r];
+      }
+      const bf16x8 db = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+      // dQ^T += K^T dS^T (rows d of this half, columns queries)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) dq[t] = mfma32x32x16(tr_frag<D>(kt, tfb, t, 0, u), db, dq[t]);
+    }
+  };
+  // Step t: publish key tile t and copy tile t + 1, the partial products, the
+  // exchange, then dS and the dQ update.  FULL steps are tiles every row of
+  // this pair sees whole; in the others a pair past its diagonal skips the
+  // work but, like every wave, passes both barriers.
+  auto step = [&](int t, auto full_tag) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    char* const kt = kbuf + (t & 1) * TILE;
+    char* const vt = vbuf + (t & 1) * TILE;
+    wait_vmem();
+    block_sync();
+    if (t + 1 < nkt) {
+      stage_rows(a.k, t + 1, kbuf + ((t + 1) & 1) * TILE);
+      stage_rows(a.v, t + 1, vbuf + ((t + 1) & 1) * TILE);
+    }
+    const int k0 = t * kBkSplit;
+    const bool active = FULL || !(CAUSAL && k0 > qw0 + qoff + 31);
+    f32x16 sc, pc;
+    if (active) {
+      scores(kt, vt, sc, pc);
+      xchg_put(xmine, lane, sc, pc);
+    }
+    lds_store_barrier();
+    if (active) {
+      xchg_add(xpeer, lane, sc, pc);
+      if constexpr (FULL) {
+        update(std::false_type{}, kt, sc, pc, k0);
+      } else {
+        const bool masked = (k0 + kBkSplit > Nk) || (CAUSAL && k0 + 31 > qw0 + qoff);
+        if (masked) update(std::true_type{}, kt, sc, pc, k0);
+        else update(std::false_type{}, kt, sc, pc, k0);
+      }
+    }
+  };
+  int t_full = min(nkt, Nk / kBkSplit);
+  if constexpr (CAUSAL) t_full = min(t_full, max(0, floor_div(qw0 + qoff - (kBkSplit - 1), kBkSplit) + 1));
+  t_full = __builtin_amdgcn_readfirstlane(t_full);
+  stage_rows(a.k, 0, kbuf);
+  stage_rows(a.v, 0, vbuf);
+  int t = 0;
+  for (; t < t_full; ++t) step(t, std::true_type{});
+  for (; t < nkt; ++t) step(t, std::false_type{});
+
+  if (myq < N) store_row_frags<DH>(a.dq + base + (int64_t)myq * rs + dh * DH, dq, hh, a.scale);
+}
+
 // ------------------------------------------------------------------ kernels
 // Waves per SIMD the dK/dV and fused kernels are compiled for (measured on
 // MI355X).  d = 64: 3 (168 registers; without the mask five dwords spill,
@@ -624,7 +997,8 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 // dQ tile, which the compiler would give about 280, spills 57 dwords, and
 // is still 1.44x faster than at one wave per SIMD).  d = 256: 1 (the dK and
 // dV accumulators of a wave alone take 256 registers; a few more spill
-// without the mask).
+// without the mask); these one-wave tiles serve d = 256 with dropout and the
+// fused grid without the mask, the column-split kernels the rest.
 template <int D, bool CAUSAL, bool DROP>
 constexpr int bwd_min_waves() {
   return D == 64 ? (CAUSAL || !DROP ? 3 : 2) : D == 128 ? 2 : 1;
@@ -636,6 +1010,22 @@ __global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL, DROP>())) void bwd_d
   int bh, kt;
   tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, false, bh, kt);   // low key tiles see the most queries
   dkdv_tile<D, CAUSAL, DROP>(a, bh, kt, smem);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kSplitWaves * 64, 2) void bwd_dkdv_split_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[dkdv_split_lds_bytes<D>()];
+  int bh, kt;
+  tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, false, bh, kt);
+  dkdv_tile_split<D, CAUSAL>(a, bh, kt, smem);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kSplitWaves * 64, 2) void bwd_dq_split_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[dq_split_lds_bytes<D>()];
+  int bh, qt;
+  tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, true, bh, qt);
+  dq_tile_split<D, CAUSAL>(a, bh, qt, smem);
 }
 
 // Single-pass backward: the dK/dV tiles also add their share of dQ with fp32
@@ -723,6 +1113,19 @@ __device__ __forceinline__ void fused_task(int id, int nt, int bhcount, bool cau
   bh = group * hpg + pos;
 }
 
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kSplitWaves * 64, 2) void bwd_fused_split_kernel(BwdArgs a) {
+  static_assert(CAUSAL, "launched under the causal mask only");
+  constexpr int LDS = dkdv_split_lds_bytes<D>() > dq_split_lds_bytes<D>() ? dkdv_split_lds_bytes<D>()
+                                                                          : dq_split_lds_bytes<D>();
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
+  bool is_kv;
+  int bh, tile;
+  fused_task(blockIdx.x, a.ntiles, a.BH, CAUSAL, is_kv, bh, tile);
+  if (is_kv) dkdv_tile_split<D, CAUSAL>(a, bh, tile, smem);
+  else dq_tile_split<D, CAUSAL>(a, bh, tile, smem);
+}
+
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL, DROP>())) void bwd_fused_kernel(BwdArgs a) {
   constexpr int LDS = dkdv_lds_bytes<D, DROP>() > dq_lds_bytes<D>() ? dkdv_lds_bytes<D, DROP>() : dq_lds_bytes<D>();
@@ -747,6 +1150,11 @@ template <int D, bool DROP = false>
 hipError_t run_dkdv(BwdArgs a, int BH, bool causal, hipStream_t st) {
   a.ntiles = (a.Nk + kKeysPerWg - 1) / kKeysPerWg;
   const dim3 grid(a.ntiles * BH);
+  if constexpr (D == 256 && !DROP) {
+    if (causal) hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, true>), grid, dim3(kSplitWaves * 64), 0, st, a);
+    else hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, false>), grid, dim3(kSplitWaves * 64), 0, st, a);
+    return hipGetLastError();
+  }
   if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, DROP>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, DROP>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
@@ -756,6 +1164,11 @@ template <int D, bool DROP = false>
 hipError_t run_dq(BwdArgs a, int BH, bool causal, hipStream_t st) {
   a.ntiles = (a.N + kQPerWg - 1) / kQPerWg;
   const dim3 grid(a.ntiles * BH);
+  if constexpr (D == 256 && !DROP) {
+    if (causal) hipLaunchKernelGGL((bwd_dq_split_kernel<D, true>), grid, dim3(kSplitWaves * 64), 0, st, a);
+    else hipLaunchKernelGGL((bwd_dq_split_kernel<D, false>), grid, dim3(kSplitWaves * 64), 0, st, a);
+    return hipGetLastError();
+  }
   if (causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, DROP>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((bwd_dq_kernel<D, false, DROP>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
@@ -766,6 +1179,15 @@ hipError_t run_fused(BwdArgs a, int BH, bool causal, hipStream_t st) {
   // Square attention only (N == Nk): key tiles == query tiles, both 128 rows.
   a.ntiles = (a.N + kKeysPerWg - 1) / kKeysPerWg;
   const dim3 grid(2 * a.ntiles * BH);
+  // d = 256 under the mask: the column-split tiles (1.26x on [2, 4096, 16,
+  // 256]).  Without the mask the split grid spills and was 2% slower than the
+  // one-wave tiles, which it keeps.
+  if constexpr (D == 256 && !DROP) {
+    if (causal) {
+      hipLaunchKernelGGL((bwd_fused_split_kernel<D, true>), grid, dim3(kSplitWaves * 64), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (causal) hipLaunchKernelGGL((bwd_fused_kernel<D, true, DROP>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((bwd_fused_kernel<D, false, DROP>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
