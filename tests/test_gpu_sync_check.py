@@ -95,6 +95,17 @@ def test_forward_backward(shape, causal):
             return dq, dk, dv
         a, b = _both(noalloc)
         _same(a, b, ("dQ noalloc", "dK noalloc", "dV noalloc"))
+    if d == 256:
+        # the separate passes (column-split tiles at this head size)
+        def separate():
+            ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device="cuda")
+            dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+            fa.fa_backward_preprocess(o, do, lse, ws)
+            fa.fa_backward_dkdv(q, k, v, do, ws, dk, dv, d ** -0.5, causal)
+            fa.fa_backward_dq(q, k, v, do, ws, dq, d ** -0.5, causal)
+            return dq, dk, dv
+        a, b = _both(separate)
+        _same(a, b, ("dQ separate", "dK separate", "dV separate"))
     say("  ok: bit-identical")
 
 
