@@ -16,7 +16,8 @@ run on.  `cpu_baseline` times the fp64 CPU oracle on one head of the same
 workload.  `forward_only` times the forward alone on the two long causal
 workloads ([4, 4096, 16, 128] and [1, 32768, 32, 128] with Q, K doubled);
 `head256` times fa_forward and fa_backward at head size 256 ([2, 4096, 16,
-256], causal and not).
+256], causal and not); `library_gemm` times the vendor library's square
+8192 GEMM in bf16 and e4m3 on the same device, as context for the spec peaks.
 
     python bench.py --copy-calibration
 
@@ -248,6 +249,39 @@ def time_fp32(fa, torch, B, N, H, d, causal, iters):
         out[name] = {"median_ms": round(med, 4), "tflops": round(tf, 2),
                      "pct_of_fp32_matrix_peak": round(100 * tf / PEAK_FP32_MATRIX_TFLOPS, 1)}
     del q, k, v, do, o, lse, dq, dk, dv, ws
+    return out
+
+
+def time_library_gemm(torch, n, iters=10):
+    """The vendor library's square GEMM (torch.matmul on bf16, torch._scaled_mm
+    on e4m3) on the same device: the rate a plain dense contraction reaches
+    under the same clock and power limits, reported beside the spec peaks."""
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    out = {"n": n}
+    one = torch.tensor(1.0, device="cuda")
+    a8 = a.to(torch.float8_e4m3fn)
+    b8 = b.to(torch.float8_e4m3fn).t().contiguous().t()   # column-major, as _scaled_mm takes it
+    calls = {"bf16": (lambda: a @ b, PEAK_BF16_TFLOPS),
+             "fp8_e4m3": (lambda: torch._scaled_mm(a8, b8, one, one, out_dtype=torch.bfloat16), PEAK_FP8_TFLOPS)}
+    st = torch.cuda.current_stream()
+    for name, (fn, peak) in calls.items():
+        try:
+            warm_up(fn, torch)
+        except Exception as e:   # an op this torch build does not provide
+            out[name] = {"error": str(e)[:120]}
+            continue
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        ev[0].record(st)
+        for i in range(iters):
+            fn()
+            ev[i + 1].record(st)
+        torch.cuda.synchronize()
+        ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+        med = ms[len(ms) // 2]
+        tf = 2 * n ** 3 / (med * 1e-3) / 1e12
+        out[name] = {"median_ms": round(med, 4), "tflops": round(tf, 1), "pct_of_peak": round(100 * tf / peak, 1)}
+    del a, b, a8, b8
     return out
 
 
@@ -614,6 +648,10 @@ def main():
             "c4": time_forward_only(fa, torch, 1, 32768, 32, 128, synth.f32(128 ** -0.5), 2.0, 4, 10),
         }
         result["forward_only"]["c2"]["note"] = "reported, not targeted (64 workgroups for 256 CUs)"
+        log("bench: library GEMM on the same device")
+        result["library_gemm"] = time_library_gemm(torch, 8192)
+        result["library_gemm"]["note"] = ("vendor GEMM (hipBLASLt through torch), context for the spec peaks; "
+                                          "not part of value")
         log("bench: head size 256")
         result["head256"] = {
             "causal": time_fwd_bwd(fa, torch, 2, 4096, 16, 256, True, 20),
