@@ -74,9 +74,11 @@ __device__ __forceinline__ i32x8 lds_read32(const char* base, uint32_t off) {
 }
 
 // Four floats to four e4m3 codes (round to nearest even), first value in the
-// lowest byte.
-__device__ __forceinline__ int pack_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+// lowest byte.  Each conversion writes one 16-bit half of its destination and
+// keeps the other; both halves are written here, so `old` (any value, e.g.
+// the register's previous contents) does not reach the result.
+__device__ __forceinline__ int pack_e4m3x4(int old, float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -209,6 +211,8 @@ __global__ __launch_bounds__(64 * kF8Waves, (D == 128 ? 3 : 4)) void fwd_fp8_ker
 #pragma unroll
   for (int t = 0; t < DT; ++t) oacc[t] = (f32x16){};
   float m_ref = -INFINITY;   // reference row max, log2 units
+  float m_thr = -INFINITY;   // m_ref + kF8Slack: a row max above it moves the reference
+  float nm = 0.f;            // exponent offset 8 - m_ref (0 while m_ref = -inf)
   float l_part = 0.f;        // this half-wave's share of sum 2^8 p
   const float c = a.c;
 
@@ -243,8 +247,10 @@ __global__ __launch_bounds__(64 * kF8Waves, (D == 128 ? 3 : 4)) void fwd_fp8_ker
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
     mx = max_halves(mx);
-    const float mcand = (mx == -INFINITY) ? -INFINITY : mx * c;
-    if (__any(mcand > m_ref + kF8Slack)) {
+    // (a row max of -inf, whose product with c could be a NaN, only occurs
+    // under the mask)
+    const float mcand = MASK ? ((mx == -INFINITY) ? -INFINITY : mx * c) : mx * c;
+    if (__any(mcand > m_thr)) {
       const float m_new = fmaxf(m_ref, mcand);
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
       l_part *= alpha;
@@ -253,8 +259,9 @@ __global__ __launch_bounds__(64 * kF8Waves, (D == 128 ? 3 : 4)) void fwd_fp8_ker
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
       m_ref = m_new;
+      m_thr = m_new + kF8Slack;
+      nm = (m_new == -INFINITY) ? 0.f : kF8PLog2 - m_new;
     }
-    const float nm = (m_ref == -INFINITY) ? 0.f : kF8PLog2 - m_ref;
     float p[32];
     float lsum[2] = {0.f, 0.f};
 #pragma unroll
@@ -268,7 +275,7 @@ __global__ __launch_bounds__(64 * kF8Waves, (D == 128 ? 3 : 4)) void fwd_fp8_ker
       }
     l_part += lsum[0] + lsum[1];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) pf[v] = pack_e4m3x4(p[4 * v], p[4 * v + 1], p[4 * v + 2], p[4 * v + 3]);
+    for (int v = 0; v < 8; ++v) pf[v] = pack_e4m3x4(pf[v], p[4 * v], p[4 * v + 1], p[4 * v + 2], p[4 * v + 3]);
   };
 
   auto pv = [&](const char* vb, const i32x8& pf) __attribute__((always_inline)) {
@@ -281,6 +288,9 @@ __global__ __launch_bounds__(64 * kF8Waves, (D == 128 ? 3 : 4)) void fwd_fp8_ker
   // into the other buffer meanwhile.  `buf_tag` is that buffer index, a
   // compile-time constant in the two-step loops.
   stage(0, 0);
+  // P as e4m3 codes; each step's packing starts from the previous step's
+  // registers (both halves of every word are overwritten).
+  i32x8 pf = {};
   auto step = [&](int kt, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
     const int cur = buf_tag;
     wait_vmem();
@@ -290,7 +300,6 @@ __global__ __launch_bounds__(64 * kF8Waves, (D == 128 ? 3 : 4)) void fwd_fp8_ker
     if (CAUSAL && k0 > qw0 + qoff + 31) return;   // no key of the tile is visible to this wave
     f32x16 s[2];
     scores(kbuf + cur * TILE, s);
-    i32x8 pf;
     softmax(mask_tag, s, k0, pf);
     pv(vbuf + cur * TILE, pf);
   };
