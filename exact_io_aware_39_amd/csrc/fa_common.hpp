@@ -300,11 +300,13 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_
   for (int r = 0; r < 10; ++r) {
     // One 32 x 32 -> 64-bit product per multiplier (v_mad_u64_u32): on
     // MI355X 1.32x the rate of separate high and low multiplies.
+    // The three-way XORs are one v_bitop3_b32 each (truth table 0x96 is
+    // a ^ b ^ c); the compiler otherwise emits two XORs.
     const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
-    x0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+    x0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), x1, k0, 0x96);
     x1 = (uint32_t)p1;
-    x2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+    x2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), x3, k1, 0x96);
     x3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
@@ -330,6 +332,17 @@ __device__ __forceinline__ bool drop_keep(const u32x4& w, uint32_t thr) {
 __device__ __forceinline__ void drop_mult8(const DropParams& dp, int bh, int row, int j0, float (&z)[8]) {
   const u32x4 w = philox4x32_10(drop_ctr0((uint32_t)j0), (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
   static_for<0, 8>([&](auto F) { z[decltype(F)::value] = drop_keep<decltype(F)::value>(w, dp.thr) ? dp.inv_keep : 0.f; });
+}
+
+// Zeroes the dropped ones of the values v[f] of keys j0 + 8 (f >> 2) + (f & 3),
+// f = 0..7, of query row `row` in head bh (j0 % 16 in {0, 4}); kept values
+// stay as they are (the caller applies inv_keep).  One generator call.
+__device__ __forceinline__ void drop_zero8(const DropParams& dp, int bh, int row, int j0, float* v) {
+  const u32x4 w = philox4x32_10(drop_ctr0((uint32_t)j0), (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
+  static_for<0, 8>([&](auto F) {
+    constexpr int f = decltype(F)::value;
+    v[f] = drop_keep<f>(w, dp.thr) ? v[f] : 0.f;
+  });
 }
 
 // Multiplier of one element (query row `row`, key `key`) of head bh.

@@ -230,8 +230,9 @@ __global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_b
   };
 
   // P = exp2(c S - m_ref) for one step, its row-sum share, and bf16 operands.
-  // With dropout the operands carry P times the keep multipliers of the step's
-  // keys (k0 ..), while the row sum takes P itself.
+  // With dropout the operands carry P of the kept elements of the step's keys
+  // (k0 ..) and 0 for the dropped ones (the keep multiplier is applied to O
+  // once, at the end), while the row sum takes P itself.
   auto exp_tile = [&](auto mask_tag, const f32x16 (&s)[2], bf16x8 (&pb)[2][2], int k0) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const float nm = -m_ref;
@@ -250,12 +251,7 @@ __global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_b
         // register 4 g + e holds key k0 + 32 j + 8 g + 4 hh + e; one call
         // serves registers 8 c .. 8 c + 7 (groups g = 2c, 2c + 1)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          float z[8];
-          drop_mult8(a.drop, bh, myq, k0 + 32 * j + 16 * c + 4 * hh, z);
-#pragma unroll
-          for (int f = 0; f < 8; ++f) p[8 * c + f] *= z[f];
-        }
+        for (int c = 0; c < 2; ++c) drop_zero8(a.drop, bh, myq, k0 + 32 * j + 16 * c + 4 * hh, p + 8 * c);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -654,10 +650,10 @@ __global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_b
     if constexpr (NB == 3) wait_vmem();   // no copy may land after the workgroup ends
   }
 
-  // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
+  // ---- epilogue: O = O_acc / l (with dropout inv_keep O_acc / l), LSE = ln2 * (m + log2 l)
   const float l = sum_halves(l_part);
   if (myq < N) {
-    const float inv = 1.f / l;
+    const float inv = (DROP ? a.drop.inv_keep : 1.f) / l;
     __bf16* orow = a.o + base + (int64_t)myq * rs;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
