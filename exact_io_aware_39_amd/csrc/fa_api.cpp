@@ -108,8 +108,10 @@ fa_status fa_forward_dropout(const void* Q, const void* K, const void* V, void* 
   if (st == FA_OK) st = check_tensors({Q, K, V, O}, {LSE});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, scale, causal};
-  return to_status(fa::launch_fwd_dropout_bf16(Q, K, V, O, LSE, s, drop_params(p_drop, seed, offset),
-                                               static_cast<hipStream_t>(stream)));
+  const fa::DropParams dp = drop_params(p_drop, seed, offset);
+  // t = 0 keeps every element with multiplier 1: the plain forward computes that.
+  if (dp.thr == 0) return to_status(fa::launch_fwd_bf16(Q, K, V, O, LSE, s, static_cast<hipStream_t>(stream)));
+  return to_status(fa::launch_fwd_dropout_bf16(Q, K, V, O, LSE, s, dp, static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_backward_dropout(const void* Q, const void* K, const void* V, const void* O,
@@ -121,8 +123,12 @@ fa_status fa_backward_dropout(const void* Q, const void* K, const void* V, const
   if (st == FA_OK) st = check_tensors({Q, K, V, O, dO, dQ, dK, dV}, {LSE, workspace});
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, scale, causal};
-  return to_status(fa::launch_bwd_dropout_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, s,
-                                               drop_params(p_drop, seed, offset),
+  const fa::DropParams dp = drop_params(p_drop, seed, offset);
+  // t = 0 keeps every element with multiplier 1: the plain backward computes that.
+  if (dp.thr == 0)
+    return to_status(fa::launch_bwd_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, s,
+                                         static_cast<hipStream_t>(stream)));
+  return to_status(fa::launch_bwd_dropout_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, s, dp,
                                                static_cast<hipStream_t>(stream)));
 }
 

@@ -274,14 +274,19 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
   // S = Q K^T and dP = dO V^T for 32-row block sb of a tile: lane = key,
   // register r = query row 32 sb + 8(r/4) + 4hh + r%4 (the row swizzle
   // repeats every 16 rows, so block sb is the lane base plus a row offset).
-  // The dP product starts from -D of each query row, so pacc ends as dP - D.
+  // The dP product starts from -D of each query row, so pacc ends as dP - D
+  // (with dropout from 0: pacc = dP).
   auto scores = [&](const char* slot, int sb, f32x16& sacc, f32x16& pacc) __attribute__((always_inline)) {
     sacc = (f32x16){};
+    if constexpr (DROP) {
+      pacc = (f32x16){};
+    } else {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 nd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (32 * sb + 8 * g4 + 4 * hh) * 4);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 nd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (32 * sb + 8 * g4 + 4 * hh) * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pacc[4 * g4 + e] = nd[e];
+        for (int e = 0; e < 4; ++e) pacc[4 * g4 + e] = nd[e];
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -309,15 +314,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
         const int g4 = 2 * u + g;
         const f32x4 nl = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + (32 * sb + 8 * g4 + 4 * hh) * 4);
         f32x4 nd;
-        float zq[4];
+        uint32_t km[4];   // keep masks (all ones: kept)
         if constexpr (DROP) {
           nd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (32 * sb + 8 * g4 + 4 * hh) * 4);
           if constexpr (D <= 128) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) zq[e] = drop_bit_mult(dbits, 4 * g4 + e, a.drop.inv_keep);
+            for (int e = 0; e < 4; ++e) km[e] = drop_bit_mask(dbits, 4 * g4 + e);
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) zq[e] = drop_mult1(a.drop, bh, qi0 + 8 * g4 + 4 * hh + e, mykey);
+            for (int e = 0; e < 4; ++e) km[e] = drop_mask1(a.drop, bh, qi0 + 8 * g4 + 4 * hh + e, mykey);
           }
         }
 #pragma unroll
@@ -330,10 +335,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
             pv = hide ? 0.f : pv;
           }
           if constexpr (DROP) {
-            // dV takes P z; dS = P (z dO.V - D) = P (z pacc + (1 - z) (-D))
-            const float z = zq[e];
-            p[4 * g + e] = pv * z;
-            ds[4 * g + e] = pv * __builtin_fmaf(z, pacc[r], (1.f - z) * nd[e]);
+            // dV takes P of the kept elements (the keep multiplier s is
+            // applied when dV is stored); dS = P (z dP - D) with pacc = dP:
+            // P (s dP - D) where kept, -P D where dropped.
+            p[4 * g + e] = __uint_as_float(km[e] & __float_as_uint(pv));
+            ds[4 * g + e] = pv * mask_select(km[e], __builtin_fmaf(a.drop.inv_keep, pacc[r], nd[e]), nd[e]);
           } else {
             p[4 * g + e] = pv;
             ds[4 * g + e] = pv * pacc[r];
@@ -463,7 +469,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
 
   if (mykey < Nk) {
     store_row_frags<D>(a.dk + kbase + (int64_t)mykey * rs, dk, hh, a.scale);
-    store_row_frags<D>(a.dv + kbase + (int64_t)mykey * rs, dv, hh, 1.f);
+    store_row_frags<D>(a.dv + kbase + (int64_t)mykey * rs, dv, hh, DROP ? a.drop.inv_keep : 1.f);
   }
 }
 
@@ -750,7 +756,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
   auto scores = [&](const char* kt, const char* vt, int j, f32x16& sacc, f32x16& pacc) {
     sacc = (f32x16){};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pacc[r] = ndval;   // so that pacc ends as dP^T - D
+    for (int r = 0; r < 16; ++r) pacc[r] = DROP ? 0.f : ndval;   // pacc ends as dP^T - D (with dropout dP^T)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       sacc = mfma32x32x16(lds_read_b128(kt, (rfb ^ (ks << 5)) + 32 * j * RB), qf[ks], sacc);
@@ -763,11 +769,11 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float ds[8];
-      float z[8];
       // registers 8 u + e: keys k0 + 32 j + 16 u + 4 hh + 8 (e >> 2) + (e & 3), one call
-      if constexpr (DROP) drop_mult8(a.drop, bh, myq, k0 + 32 * j + 16 * u + 4 * hh, z);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      u32x4 w;
+      if constexpr (DROP) w = drop_word8(a.drop, bh, myq, k0 + 32 * j + 16 * u + 4 * hh);
+      static_for<0, 8>([&](auto E) {
+        constexpr int e = decltype(E)::value;
         const int r = 8 * u + e;
         float pv = fast_exp2(__builtin_fmaf(sacc[r], c, nl2));
         if constexpr (MASK) {
@@ -776,12 +782,13 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
           pv = hide ? 0.f : pv;
         }
         if constexpr (DROP) {
-          const float zz = z[e];
-          ds[e] = pv * __builtin_fmaf(zz, pacc[r], (1.f - zz) * ndval);
+          // dS^T = P (z dP - D) with pacc = dP: P (s dP - D) where kept, -P D
+          // where dropped
+          ds[e] = pv * (drop_keep<e>(w, a.drop.thr) ? __builtin_fmaf(a.drop.inv_keep, pacc[r], ndval) : ndval);
         } else {
           ds[e] = pv * pacc[r];
         }
-      }
+      });
       const bf16x8 db = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
       // dQ^T += K^T dS^T (rows d, columns queries)
 #pragma unroll

@@ -327,11 +327,11 @@ __device__ __forceinline__ bool drop_keep(const u32x4& w, uint32_t thr) {
   else return (w[F >> 1] << 16) >= thr;
 }
 
-// Multipliers (0 or inv_keep) of keys j0 + 8 (f >> 2) + (f & 3), f = 0..7,
-// of query row `row` in head bh (j0 % 16 in {0, 4}): one generator call.
-__device__ __forceinline__ void drop_mult8(const DropParams& dp, int bh, int row, int j0, float (&z)[8]) {
-  const u32x4 w = philox4x32_10(drop_ctr0((uint32_t)j0), (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
-  static_for<0, 8>([&](auto F) { z[decltype(F)::value] = drop_keep<decltype(F)::value>(w, dp.thr) ? dp.inv_keep : 0.f; });
+// The generator call that serves keys j0 + 8 (f >> 2) + (f & 3), f = 0..7, of
+// query row `row` in head bh (j0 % 16 in {0, 4}); drop_keep<f> reads key f's
+// decision from it.
+__device__ __forceinline__ u32x4 drop_word8(const DropParams& dp, int bh, int row, int j0) {
+  return philox4x32_10(drop_ctr0((uint32_t)j0), (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
 }
 
 // Zeroes the dropped ones of the values v[f] of keys j0 + 8 (f >> 2) + (f & 3),
@@ -345,12 +345,13 @@ __device__ __forceinline__ void drop_zero8(const DropParams& dp, int bh, int row
   });
 }
 
-// Multiplier of one element (query row `row`, key `key`) of head bh.
-__device__ __forceinline__ float drop_mult1(const DropParams& dp, int bh, int row, int key) {
+// Keep decision of one element (query row `row`, key `key`) of head bh, as
+// a mask of all ones (kept) or zero.
+__device__ __forceinline__ uint32_t drop_mask1(const DropParams& dp, int bh, int row, int key) {
   const u32x4 w = philox4x32_10(drop_ctr0((uint32_t)key), (uint32_t)row, (uint32_t)bh, dp.offset, dp.key0, dp.key1);
   const int f = ((key >> 1) & 4) | (key & 3);
   const uint32_t x = (f >> 1) == 0 ? w[0] : (f >> 1) == 1 ? w[1] : (f >> 1) == 2 ? w[2] : w[3];
-  return ((f & 1) ? x : (x << 16)) >= dp.thr ? dp.inv_keep : 0.f;
+  return ((f & 1) ? x : (x << 16)) >= dp.thr ? 0xFFFFFFFFu : 0u;
 }
 
 // Keep bits of 16 query rows at this lane's key, for layouts where lane l
@@ -388,10 +389,14 @@ __device__ __forceinline__ uint32_t drop_bits16(const DropParams& dp, int bh, in
   return m;
 }
 
-// Multiplier of keep bit r of a drop_bits16 result (0 or inv_keep).
-__device__ __forceinline__ float drop_bit_mult(uint32_t bits, int r, float inv_keep) {
-  const uint32_t all = (uint32_t)((int32_t)(bits << (31 - r)) >> 31);
-  return __uint_as_float(all & __float_as_uint(inv_keep));
+// Keep bit r of a drop_bits16 result as a mask of all ones or zero.
+__device__ __forceinline__ uint32_t drop_bit_mask(uint32_t bits, int r) {
+  return (uint32_t)((int32_t)(bits << (31 - r)) >> 31);
+}
+
+// Bitwise select of two floats by such a mask (one v_bfi_b32).
+__device__ __forceinline__ float mask_select(uint32_t m, float kept, float dropped) {
+  return __uint_as_float((m & __float_as_uint(kept)) | (~m & __float_as_uint(dropped)));
 }
 
 }  // namespace fa

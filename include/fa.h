@@ -108,7 +108,9 @@ fa_status fa_forward_cross(const void* Q, const void* K, const void* V, void* O,
  * (query row i, key j) of head b*H + h is kept when field
  * 4 ((j / 8) % 2) + j % 4 of the call on the counter
  * (2 (j / 16) + (j / 4) % 2, i, b*H + h, offset) is >= t.
- * 0 <= p_drop < 1 (else FA_ERR_INVALID_ARG); p_drop = 0 keeps everything.
+ * 0 <= p_drop < 1 (else FA_ERR_INVALID_ARG); p_drop = 0 keeps everything: a
+ * rate that rounds to t = 0 runs exactly what fa_forward (and, for the
+ * backward, fa_backward) runs.
  * Same layouts, checks and limits as fa_forward (square attention).
  */
 fa_status fa_forward_dropout(const void* Q, const void* K, const void* V, void* O, float* LSE,

@@ -61,7 +61,16 @@ def test_dropout_offset_and_head_groups():
     _run((2, 300, 4, 64), 7100, True, 0.2, offset=77)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_dropout_smallest_rate(d):
+    """p = 2^-16 (threshold t = 1, the smallest rate that runs the dropout
+    kernels: almost every element kept, multiplier 65536/65535) against the
+    oracle; p = 0 runs the plain kernels instead (next test)."""
+    _run((2, 300, 2, d), 7250 + d, True, 2.0 ** -16)
+
+
 def test_dropout_p0_is_plain_attention():
+    """A rate that rounds to t = 0 runs what fa_forward / fa_backward run."""
     require_gpu()
     dev, f64 = inputs((1, 200, 2, 64), "bf16", 7200, with_do=True)
     o, lse = fa.forward_dropout(dev["q"], dev["k"], dev["v"], 0.0, SEED, scale=0.125, causal=True)
