@@ -78,6 +78,28 @@ def check(got, ref, dtype, what):
     return float(err.max()), float(err.mean())
 
 
+def dropout_d_terms(q, k, do, o_ref, scale, causal):
+    """Bounds on how far the bf16 rounding of the stored O moves dQ and dK
+    (fp64 arrays [N, d] of one head; o_ref the exact dropout output).
+
+    The backward takes D_i = sum_c dO_ic O_ic from the O the forward stored in
+    bf16, O_ic + e_ic with |e_ic| <= 2^-9 |O_ic| (round to nearest), so D_i
+    is off by up to eps_i = 2^-9 sum_c |dO_ic| |O_ic|.  dS = P * (Z * dP - D)
+    then carries -P_ij times that error: dQ_i moves by at most scale eps_i
+    sum_j P_ij |K_j| and dK_j by at most scale sum_i P_ij eps_i |Q_i|.  Where
+    a row sees few keys the exact dS is a small difference of large terms (a
+    causal row that sees one key: s dP - D = 0 exactly), so this term can
+    exceed the plain bars; without dropout such a row's O is a bf16 value of
+    V and is stored exactly."""
+    from oracle.attention import scores, softmax_rows   # test infrastructure only
+    q, k, do, o_ref = (np.asarray(x, np.float64) for x in (q, k, do, o_ref))
+    pm = softmax_rows(scores(q, k, scale, causal))[0]
+    eps = 1.01 * 2.0 ** -9 * (np.abs(do) * np.abs(o_ref)).sum(axis=1)
+    dq_term = abs(scale) * eps[:, None] * (pm @ np.abs(k))
+    dk_term = abs(scale) * (pm.T @ (eps[:, None] * np.abs(q)))
+    return dq_term, dk_term
+
+
 def count_over(got, ref, bar=BF16_MAX):
     """Number of elements whose abs error exceeds `bar` (a report, not a check)."""
     return int((np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64)) > bar).sum())
@@ -91,19 +113,21 @@ def check_lse(got, ref, what):
     return float(err.max())
 
 
-def check_dropout(got, ref, s, what):
+def check_dropout(got, ref, s, what, d_term=None):
     """Bar for outputs of the dropout entry points, s = the scale of kept
     probabilities: every kept term is multiplied by s, so outputs grow by up to
     s and so does the bf16 rounding of them (half an ulp is up to 2^-9 |x|).
     An element may differ from the oracle by 2^-8 |ref| (the rounding of the
-    result, with margin) plus s times the plain path's absolute bar (2e-2);
-    the mean error may reach s times the plain mean bar plus 2^-8 times the
-    mean |ref|.  A wrong mask element moves a result by a whole term."""
+    result, with margin) plus s times the plain path's absolute bar (2e-2),
+    plus, for dQ and dK, `d_term` (dropout_d_terms: what the bf16 rounding
+    of the stored O moves them by through D = rowsum(dO * O)); the mean error
+    may reach s times the plain mean bar plus 2^-8 times the mean |ref|.  A
+    wrong mask element moves a result by a whole term."""
     got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
     assert np.isfinite(got).all(), f"{what}: non-finite values"
     err = np.abs(got - ref)
-    over = err - 2.0 ** -8 * np.abs(ref)
+    over = err - 2.0 ** -8 * np.abs(ref) - (0.0 if d_term is None else d_term)
     assert over.max() <= BF16_MAX * s, f"{what}: max abs err {err.max():.3e} ({over.max():.3e} beyond 2^-8 |ref|)"
     mean_bar = BF16_MEAN * s + 2.0 ** -8 * np.abs(ref).mean()
     assert err.mean() <= mean_bar, f"{what}: mean abs err {err.mean():.3e} > {mean_bar:.2e}"

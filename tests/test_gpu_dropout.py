@@ -4,7 +4,9 @@ The oracle replays the mask from (head, query row, key, seed, offset) with its
 own Philox4x32-10 (oracle/dropout.py), so the comparison is element by element
 against the same mask.  Bars: `gpu_helpers.check_dropout` with s =
 keep_scale(p) (about 1 / (1 - p)), the multiplier of every kept term: 2^-8
-|ref| plus s times the plain path's bars.  A wrong mask element moves a short
+|ref| plus s times the plain path's bars, plus for dQ and dK the bound of
+`gpu_helpers.dropout_d_terms` on what the bf16 rounding of the stored O moves
+them by through D = rowsum(dO * O).  A wrong mask element moves a short
 row's result by a whole term, far above these bars; the bit-exact mask test
 covers long rows.
 """
@@ -15,15 +17,15 @@ import torch
 import exact_io_aware_39_amd as fa
 import oracle.dropout as drop
 import synth
-from gpu_helpers import check_dropout, check_lse, inputs, require_gpu, say, to64
+from gpu_helpers import check_dropout, check_lse, dropout_d_terms, inputs, require_gpu, say, to64
 
 pytestmark = pytest.mark.gpu
 
 SEED = 0x5EED_0000_1234_ABCD
 
 
-def check(got, ref, p, what):
-    check_dropout(got, ref, drop.keep_scale(p), what)
+def check(got, ref, p, what, d_term=None):
+    check_dropout(got, ref, drop.keep_scale(p), what, d_term)
 
 
 def _run(shape, seed, causal, p, offset=0, heads=None, check_rows=None):
@@ -44,8 +46,9 @@ def _run(shape, seed, causal, p, offset=0, heads=None, check_rows=None):
         check(to64(o[b, :, h]), o_r, p, f"dropout O b={b} h={h}")
         check_lse(to64(lse[b, h]), lse_r, f"dropout LSE b={b} h={h}")
         dq_r, dk_r, dv_r, _ = drop.backward(q, k, v, do, scale, causal, keep, p)
-        for name, got, ref in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
-            check(to64(got[b, :, h]), ref, p, f"dropout {name} b={b} h={h}")
+        dq_t, dk_t = dropout_d_terms(q, k, do, o_r, scale, causal)
+        for name, got, ref, t in (("dQ", dq, dq_r, dq_t), ("dK", dk, dk_r, dk_t), ("dV", dv, dv_r, None)):
+            check(to64(got[b, :, h]), ref, p, f"dropout {name} b={b} h={h}", t)
     return dev, (o, lse), (dq, dk, dv)
 
 

@@ -20,7 +20,7 @@ import oracle.dropout as drop
 import oracle.fp8 as fp8
 import synth
 from fp8_bounds import loose_bound, lse_bound
-from gpu_helpers import check, check_dropout, check_lse, require_gpu, say, to64, to_dev
+from gpu_helpers import check, check_dropout, check_lse, dropout_d_terms, require_gpu, say, to64, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -133,8 +133,9 @@ def test_sweep(c):
             refs = drop.backward(qh, kh, vh, f64["do"][b, :, h], scale, causal, keep, c["p"])[:3]
             s = drop.keep_scale(c["p"])
             check_dropout(o64[b, :, h], o_r, s, f"O {what}")
-            for name, g, r in zip(("dQ", "dK", "dV"), g64, refs):
-                check_dropout(g[b, :, h], r, s, f"{name} {what}")
+            terms = dropout_d_terms(qh, kh, f64["do"][b, :, h], o_r, scale, causal) + (None,)
+            for name, g, r, t in zip(("dQ", "dK", "dV"), g64, refs, terms):
+                check_dropout(g[b, :, h], r, s, f"{name} {what}", t)
         else:
             if kind in ("cross", "decode"):
                 o_r, lse_r = ora.decode(qh, kh, vh, scale, causal)
