@@ -27,10 +27,10 @@
 //                 one scalar per lane, and dS^T feeds dQ^T += K^T dS^T directly.
 // fa_backward runs 2 and 3 as one grid (bwd_fused) ordered heaviest first, so
 // the two passes share one tail; the split entry points launch them apart.
-// At head size 256 (without dropout) the separate passes, and the fused grid
-// under the causal mask, run column-split forms of both tiles: eight waves,
-// each pair holding the same rows and half of the columns, whose partial
-// scores meet in LDS (two waves per SIMD instead of one).
+// At head size 256 (without dropout) both passes run eight-wave tiles whose
+// wave pairs hold the same rows (two waves per SIMD instead of one): dQ by a
+// score wave and a dQ wave, dK/dV by a P wave and a dS wave without the mask
+// and by column halves under it (each the faster form there on MI355X).
 // Both passes stage their streamed tiles with buffer -> LDS copies into two
 // LDS slots.  At head size 64 these plain loops at three waves per SIMD
 // measured faster than software-pipelined forms (the score products of the
@@ -473,6 +473,220 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
   }
 }
 
+// ------------------------------------------------------------------ d = 256: wave pairs with split roles
+// At d = 256 the dK and dV accumulators of 32 keys alone take 256 registers
+// of a wave, which leaves one wave per SIMD and nothing to hide its
+// latencies.  Here eight waves share the 128-key tile: waves w and w + 4 hold
+// the same 32 keys (two waves per SIMD) and divide the one-wave tile's work
+// by role:
+//  * the P wave (w) holds K, forms S = Q K^T and P = exp2(c S - LSE log2 e),
+//    hands P to its partner through LDS as fp32 and accumulates dV^T += dO^T P;
+//  * the dS wave (w + 4) holds V, forms dP - D = dO V^T - D, and one step
+//    later, with that step's P from its partner, dS = P (dP - D) and
+//    dK^T += Q^T dS.
+// Every product and elementwise operation is the one-wave tile's, in the same
+// order, so dK and dV are bitwise those of the one-wave tile.  The dS wave
+// runs one step behind, which puts the two waves of a SIMD out of phase (the
+// exponentials of one beside the products of the other), and the query tiles
+// rotate through three LDS slots: tile s + 1 is copied while the P wave reads
+// tile s and the dS wave tiles s - 1 and s.  One barrier per step.  The
+// launchers take this tile without the causal mask; under it the
+// column-split tile below measured faster.
+constexpr int kPairWaves = 8;
+constexpr int kPBytes = 4 * 64 * 16 * 4;   // P of one step: 4 pairs x 64 lanes x 16 floats
+
+template <int D>
+constexpr int dkdv_pair_lds_bytes() { return 3 * (2 * 32 * D * 2 + 512) + 2 * kPBytes; }
+
+// dK, dV of key tile kt of head bh by wave pairs (eight waves, 32 query rows
+// per step).
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dkdv_tile_pair(const BwdArgs& a, int bh, int kt, char* smem) {
+  constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
+  constexpr int kBq = 32;
+  constexpr int TILE = kBq * RB;            // one Q or dO tile
+  constexpr int CPW = TILE / 1024 / kPairWaves;
+  constexpr int SLOT = 2 * TILE + 512;      // Q, dO, then 64 floats of -LSE log2 e and of -D
+  static_assert(CPW * kPairWaves * 1024 == TILE, "the copies cover the tile");
+  static_assert(3 * SLOT + 2 * kPBytes == dkdv_pair_lds_bytes<D>(), "LDS layout");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int kg = wave & 3;                                        // key group
+  const int role = __builtin_amdgcn_readfirstlane(wave >> 2);    // 0: P wave, 1: dS wave
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int N = a.N, Nk = a.Nk, qoff = a.qoff;
+  const int64_t rs = (int64_t)a.H * D;
+  const int64_t base = ((int64_t)b * N * a.H + h) * D;      // Q, dO
+  const int64_t kbase = ((int64_t)b * Nk * a.H + h) * D;    // K, V, dK, dV
+  const float* dstat = a.ws + (int64_t)bh * N;
+  const float* nlstat = a.ws + a.bhn + (int64_t)bh * N;
+
+  const int k0 = kt * kKeysPerWg;
+  const int kw0 = k0 + 32 * kg;
+  const int mykey = kw0 + l32;
+  const int64_t krow = kbase + (int64_t)min(mykey, Nk - 1) * rs;
+
+  const int qstart = CAUSAL ? max(0, k0 - qoff) : 0;
+  const int nsteps = (N - qstart + kBq - 1) / kBq;
+
+  auto slot_of = [&](int s) { return smem + (s % 3) * SLOT; };
+  // P of step s: float4 64 g4 + lane of this pair's area holds registers
+  // 4 g4 .. 4 g4 + 3 of the lane (the same lane layout in both waves).
+  auto pbuf = [&](int s) {
+    return reinterpret_cast<f32x4*>(smem + 3 * SLOT + (s & 1) * kPBytes) + kg * 4 * 64;
+  };
+  uint32_t voff[CPW];
+  stage_offsets<D, CPW, kPairWaves>(voff, wave, lane, rs);
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  auto stage = [&](int s) {
+    char* slot = slot_of(s);
+    const int qi0 = qstart + s * kBq;
+    const int rows = min(N - qi0, kBq);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + base + (int64_t)qi0 * rs, (uint32_t)(rows * rs * 2));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.dout + base + (int64_t)qi0 * rs, (uint32_t)(rows * rs * 2));
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      buffer_to_lds16(rq, voff[i], slot + (wu + kPairWaves * i) * 1024);
+      buffer_to_lds16(rg, voff[i], slot + TILE + (wu + kPairWaves * i) * 1024);
+    }
+    if (wu == 0)
+      buffer_to_lds4(make_rsrc(nlstat + qi0, (uint32_t)(rows * 4)), lane * 4, slot + 2 * TILE);
+    else if (wu == 1)
+      buffer_to_lds4(make_rsrc(dstat + qi0, (uint32_t)(rows * 4)), lane * 4, slot + 2 * TILE + 256);
+  };
+  // Start of step s for every wave: tile s published, tile s + 1 on its way.
+  auto sync_stage = [&](int s) {
+    wait_vmem();
+    block_sync();
+    if (s + 1 < nsteps) stage(s + 1);
+  };
+  const uint32_t rfb = row_frag_base<D>(lane);
+  const uint32_t tfb = tr_frag_base<D>(lane);
+  const float c = a.c;
+
+  // Sections of steps (see dkdv_tile): [0, s_vis) no row sees this pair's
+  // keys, [s_vis, s_unm) masked, [s_unm, nfull) unmasked, [nfull, nsteps)
+  // masked (rows past N).
+  const int nfull = (N - qstart) / kBq;
+  int s_vis = 0, s_unm = 0;
+  if constexpr (CAUSAL) {
+    s_vis = min(nsteps, max(0, ceil_div(kw0 - qoff - (kBq - 1) - qstart, kBq)));
+    s_unm = min(nsteps, max(s_vis, ceil_div(kw0 + 31 - qoff - qstart, kBq)));
+    s_vis = __builtin_amdgcn_readfirstlane(s_vis);
+    s_unm = __builtin_amdgcn_readfirstlane(s_unm);
+  }
+  stage(0);
+  if (role == 0) {
+    // K^T as B operand: this lane's key, chunk 2 ks + hh.
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(a.k + krow + (2 * ks + hh) * 8);
+    f32x16 dv[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) dv[t] = (f32x16){};
+    // S (lane = key, register r = query row 8(r/4) + 4hh + r%4), P, its
+    // publication and the dV update for step s.
+    auto p_step = [&](int s, auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const char* slot = slot_of(s);
+      const int qi0 = qstart + s * kBq;
+      f32x16 sacc = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc = mfma32x32x16(lds_read_b128(slot, rfb ^ (ks << 5)), kf[ks], sacc);
+      f32x4* const po = pbuf(s);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float p[8];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int g4 = 2 * u + g;
+          const f32x4 nl = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + (8 * g4 + 4 * hh) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pv = fast_exp2(__builtin_fmaf(sacc[4 * g4 + e], c, nl[e]));
+            if constexpr (MASK) {
+              const int qrow = qi0 + 8 * g4 + 4 * hh + e;
+              const bool hide = qrow >= N || (CAUSAL && mykey > qrow + qoff);
+              pv = hide ? 0.f : pv;
+            }
+            p[4 * g + e] = pv;
+          }
+          po[64 * g4 + lane] = (f32x4){p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+        }
+        const bf16x8 pb = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        // dV^T += dO^T P (rows d, columns keys)
+#pragma unroll
+        for (int t = 0; t < DT; ++t) dv[t] = mfma32x32x16(tr_frag<D>(slot + TILE, tfb, t, 0, u), pb, dv[t]);
+      }
+    };
+    int s = 0;
+    for (; s < s_vis; ++s) sync_stage(s);
+    for (; s < s_unm; ++s) { sync_stage(s); p_step(s, std::true_type{}); }
+    for (; s < nfull; ++s) { sync_stage(s); p_step(s, std::false_type{}); }
+    for (; s < nsteps; ++s) { sync_stage(s); p_step(s, std::true_type{}); }
+    block_sync();   // the dS wave reads the last step's P after this barrier
+    if (mykey < Nk) store_row_frags<D>(a.dv + krow, dv, hh, 1.f);
+  } else {
+    bf16x8 vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) vf[ks] = *reinterpret_cast<const bf16x8*>(a.v + krow + (2 * ks + hh) * 8);
+    f32x16 dk[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) dk[t] = (f32x16){};
+    f32x16 pacc;   // dP - D of the step whose P has not arrived yet
+    // dP - D for step s: the product starts from -D of each query row.
+    auto dp_step = [&](int s) __attribute__((always_inline)) {
+      const char* slot = slot_of(s);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 nd = *reinterpret_cast<const f32x4*>(slot + 2 * TILE + 256 + (8 * g4 + 4 * hh) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pacc[4 * g4 + e] = nd[e];
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        pacc = mfma32x32x16(lds_read_b128(slot + TILE, rfb ^ (ks << 5)), vf[ks], pacc);
+    };
+    // dS = P (dP - D) with step s's P from the partner, and the dK update.
+    auto dk_step = [&](int s) __attribute__((always_inline)) {
+      const char* slot = slot_of(s);
+      const f32x4* const pi = pbuf(s);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float ds[8];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int g4 = 2 * u + g;
+          const f32x4 pv = pi[64 * g4 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[4 * g + e] = pv[e] * pacc[4 * g4 + e];
+        }
+        const bf16x8 db = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+        // dK^T += Q^T dS (rows d, columns keys)
+#pragma unroll
+        for (int t = 0; t < DT; ++t) dk[t] = mfma32x32x16(tr_frag<D>(slot, tfb, t, 0, u), db, dk[t]);
+      }
+    };
+    int s = 0;
+    for (; s < s_vis; ++s) sync_stage(s);
+    if (s < nsteps) {
+      sync_stage(s);
+      dp_step(s);
+      for (++s; s < nsteps; ++s) {
+        sync_stage(s);
+        dk_step(s - 1);
+        dp_step(s);
+      }
+      block_sync();
+      dk_step(nsteps - 1);
+    } else {
+      block_sync();
+    }
+    if (mykey < Nk) store_row_frags<D>(a.dk + krow, dk, hh, a.scale);
+  }
+}
+
 // ------------------------------------------------------------------ d = 256: columns split over wave pairs
 // At d = 256 the dK and dV accumulators of 32 keys alone take 256 registers
 // of a wave, which leaves one wave per SIMD and nothing to hide one wave's
@@ -481,7 +695,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs& a, int bh, int kt, char
 // 128 .. 255 of K, V, dK and dV (two waves per SIMD).  Each forms its
 // columns' part of S = Q K^T and dP = dO V^T, the two parts meet in LDS as
 // fp32, and both waves go on from the same sums (a + b and b + a are the
-// same fp32 value); each then updates its own columns of dV and dK.
+// same fp32 value); each then updates its own columns of dV and dK.  The
+// launchers take this tile under the causal mask.
 constexpr int kSplitWaves = 8;
 constexpr int kXchgBytes = kSplitWaves * 64 * 32 * 4;   // 32 floats per lane and wave
 
@@ -843,157 +1058,163 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
   if (myq < N) store_row_frags<D>(a.dq + base + (int64_t)myq * rs, dq, hh, a.scale);
 }
 
-// dQ of query tile qtile of head bh with the columns split over wave pairs
-// (eight waves; waves w and w + 4 hold the same 32 queries, wave w columns
-// 0 .. D/2 - 1 of Q, dO and dQ, wave w + 4 the rest).  K and V go through LDS
-// 32 keys per step (two 32 KB K/V slot pairs beside the 64 KB exchange).
-constexpr int kBkSplit = 32;
+// dQ of query tile qtile of head bh by wave pairs (eight waves; waves w and
+// w + 4 hold the same 32 queries).  The score wave (w) holds Q and dO and
+// does all of the one-wave tile's work up to dS^T: S^T = K Q^T, dP^T - D =
+// V dO^T - D, P^T and dS^T = P^T (dP^T - D), rounded to bf16 as the product
+// takes it, which it hands to its partner through LDS.  The dQ wave (w + 4)
+// holds the dQ accumulators and, one step behind, adds dQ^T += K^T dS^T.
+// The products and elementwise operations are the one-wave tile's in the
+// same order (bitwise the same dQ).  K and V rotate through three 32-key
+// slot pairs: the dQ wave reads K of the step before the score wave's.
+constexpr int kBkPair = 32;
+constexpr int kDsBytes = 4 * 64 * 32;   // dS^T of one step: 4 pairs x 64 lanes x 16 bf16
 
 template <int D>
-constexpr int dq_split_lds_bytes() { return 2 * 2 * kBkSplit * D * 2 + kXchgBytes; }
+constexpr int dq_pair_lds_bytes() { return 3 * 2 * kBkPair * D * 2 + 2 * kDsBytes; }
 
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void dq_tile_split(const BwdArgs& a, int bh, int qtile, char* smem) {
-  constexpr int DH = D / 2;
-  constexpr int KS = DH / 16, DT = DH / 32, RB = D * 2;
-  constexpr int TILE = kBkSplit * RB;
-  constexpr int CPW = TILE / 1024 / kSplitWaves;
-  static_assert(CPW * kSplitWaves * 1024 == TILE, "the copies cover the tile");
-  static_assert(4 * TILE + kXchgBytes == dq_split_lds_bytes<D>(), "LDS layout");
-  char* const kbuf = smem;                 // slots 0, 1
-  char* const vbuf = smem + 2 * TILE;      // slots 0, 1
+__device__ __forceinline__ void dq_tile_pair(const BwdArgs& a, int bh, int qtile, char* smem) {
+  constexpr int KS = D / 16, DT = D / 32, RB = D * 2;
+  constexpr int TILE = kBkPair * RB;       // one K or V tile
+  constexpr int CPW = TILE / 1024 / kPairWaves;
+  static_assert(CPW * kPairWaves * 1024 == TILE, "the copies cover the tile");
+  static_assert(6 * TILE + 2 * kDsBytes == dq_pair_lds_bytes<D>(), "LDS layout");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
-  const int qg = wave & 3;                                       // query group
-  const int dh = __builtin_amdgcn_readfirstlane(wave >> 2);     // column half
+  const int qg = wave & 3;                                        // query group
+  const int role = __builtin_amdgcn_readfirstlane(wave >> 2);    // 0: score wave, 1: dQ wave
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.N, Nk = a.Nk, qoff = a.qoff;
   const int64_t rs = (int64_t)a.H * D;
   const int64_t base = ((int64_t)b * N * a.H + h) * D;      // Q, dO, dQ
   const int64_t kbase = ((int64_t)b * Nk * a.H + h) * D;    // K, V
-  f32x4* const xmine = reinterpret_cast<f32x4*>(smem + 4 * TILE) + wave * 8 * 64;
-  const f32x4* const xpeer = reinterpret_cast<const f32x4*>(smem + 4 * TILE) + (wave ^ 4) * 8 * 64;
 
   const int q0 = qtile * kQPerWg;
   const int qw0 = q0 + 32 * qg;
   const int myq = qw0 + l32;
   const int qc = min(myq, N - 1);
 
-  bf16x8 qf[KS], gf[KS];
-  {
-    const int64_t qr = base + (int64_t)qc * rs + dh * DH;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qr + (2 * ks + hh) * 8);
-      gf[ks] = *reinterpret_cast<const bf16x8*>(a.dout + qr + (2 * ks + hh) * 8);
-    }
-  }
-  const float nl2 = a.ws[a.bhn + (int64_t)bh * N + qc];
-  const float ndval = a.ws[(int64_t)bh * N + qc];   // -D of this lane's query
-  const float nd_half = dh == 0 ? ndval : 0.f;       // half 0 carries it
-
-  f32x16 dq[DT];
-#pragma unroll
-  for (int t = 0; t < DT; ++t) dq[t] = (f32x16){};
-
   const int kend = CAUSAL ? min(Nk, q0 + qoff + kQPerWg) : Nk;
-  const int nkt = (kend + kBkSplit - 1) / kBkSplit;
+  const int nkt = (kend + kBkPair - 1) / kBkPair;
 
+  auto slot_of = [&](int t) { return smem + (t % 3) * (2 * TILE); };   // K, then V
+  // dS^T of step t: 16-byte unit 64 u + lane of this pair's area holds the
+  // bf16 operand of half u (registers 8 u .. 8 u + 7) of the lane.
+  auto dsbuf = [&](int t) {
+    return reinterpret_cast<bf16x8*>(smem + 6 * TILE + (t & 1) * kDsBytes) + qg * 2 * 64;
+  };
   uint32_t voff[CPW];
-  stage_offsets<D, CPW, kSplitWaves>(voff, wave, lane, rs);
+  stage_offsets<D, CPW, kPairWaves>(voff, wave, lane, rs);
   const int wu = __builtin_amdgcn_readfirstlane(wave);
-  auto stage_rows = [&](const __bf16* src, int t, char* dst) {
-    const int rows = min(Nk - t * kBkSplit, kBkSplit);
-    const __amdgpu_buffer_rsrc_t rsrc =
-        make_rsrc(src + kbase + (int64_t)t * kBkSplit * rs, (uint32_t)(rows * rs * 2));
+  auto stage = [&](int t) {
+    char* slot = slot_of(t);
+    const int rows = min(Nk - t * kBkPair, kBkPair);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kbase + (int64_t)t * kBkPair * rs, (uint32_t)(rows * rs * 2));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kbase + (int64_t)t * kBkPair * rs, (uint32_t)(rows * rs * 2));
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) buffer_to_lds16(rsrc, voff[i], dst + (wu + kSplitWaves * i) * 1024);
-  };
-
-  // Bases moved to this wave's columns (see dkdv_tile_split).
-  const uint32_t rfb = row_frag_base<D>(lane) + (uint32_t)(dh * DH * 2);
-  const uint32_t tfb = tr_frag_base<D>(lane) + (uint32_t)(dh * DH * 2);
-  // This half's part of S^T = K Q^T and dP^T = V dO^T (lane = query,
-  // register r = key 8(r/4) + 4hh + r%4 of the step); half 0's dP^T starts
-  // from -D, so the sum of the halves is dP^T - D.
-  auto scores = [&](const char* kt, const char* vt, f32x16& sacc, f32x16& pacc) __attribute__((always_inline)) {
-    sacc = (f32x16){};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) pacc[r] = nd_half;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      sacc = mfma32x32x16(lds_read_b128(kt, rfb ^ (ks << 5)), qf[ks], sacc);
-      pacc = mfma32x32x16(lds_read_b128(vt, rfb ^ (ks << 5)), gf[ks], pacc);
+    for (int i = 0; i < CPW; ++i) {
+      buffer_to_lds16(rk, voff[i], slot + (wu + kPairWaves * i) * 1024);
+      buffer_to_lds16(rv, voff[i], slot + TILE + (wu + kPairWaves * i) * 1024);
     }
   };
-  const float c = a.c;
-  auto update = [&](auto mask_tag, const char* kt, const f32x16& sacc, const f32x16& pacc, int k0)
-      __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float ds[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * u + e;
-        float pv = fast_exp2(__builtin_fmaf(sacc[r], c, nl2));
-        if constexpr (MASK) {
-          const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool hide = key >= Nk || (CAUSAL && key > myq + qoff);
-          pv = hide ? 0.f : pv;
-        }
-        ds[e] = pv * pacc[r];
-      }
-      const bf16x8 db = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-      // dQ^T += K^T dS^T (rows d of this half, columns queries)
-#pragma unroll
-      for (int t = 0; t < DT; ++t) dq[t] = mfma32x32x16(tr_frag<D>(kt, tfb, t, 0, u), db, dq[t]);
-    }
-  };
-  // Step t: publish key tile t and copy tile t + 1, the partial products, the
-  // exchange, then dS and the dQ update.  FULL steps are tiles every row of
-  // this pair sees whole; in the others a pair past its diagonal skips the
-  // work but, like every wave, passes both barriers.
-  auto step = [&](int t, auto full_tag) __attribute__((always_inline)) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    char* const kt = kbuf + (t & 1) * TILE;
-    char* const vt = vbuf + (t & 1) * TILE;
+  auto sync_stage = [&](int t) {
     wait_vmem();
     block_sync();
-    if (t + 1 < nkt) {
-      stage_rows(a.k, t + 1, kbuf + ((t + 1) & 1) * TILE);
-      stage_rows(a.v, t + 1, vbuf + ((t + 1) & 1) * TILE);
-    }
-    const int k0 = t * kBkSplit;
-    const bool active = FULL || !(CAUSAL && k0 > qw0 + qoff + 31);
-    f32x16 sc, pc;
-    if (active) {
-      scores(kt, vt, sc, pc);
-      xchg_put(xmine, lane, sc, pc);
-    }
-    lds_store_barrier();
-    if (active) {
-      xchg_add(xpeer, lane, sc, pc);
-      if constexpr (FULL) {
-        update(std::false_type{}, kt, sc, pc, k0);
-      } else {
-        const bool masked = (k0 + kBkSplit > Nk) || (CAUSAL && k0 + 31 > qw0 + qoff);
-        if (masked) update(std::true_type{}, kt, sc, pc, k0);
-        else update(std::false_type{}, kt, sc, pc, k0);
+    if (t + 1 < nkt) stage(t + 1);
+  };
+  const uint32_t rfb = row_frag_base<D>(lane);
+  const uint32_t tfb = tr_frag_base<D>(lane);
+  const float c = a.c;
+
+  // Steps [0, t_full) are seen whole by every row of the pair; [t_full,
+  // t_act) are masked (the diagonal, keys past Nk); from t_act on no row of
+  // the pair sees the step's keys.
+  int t_full = min(nkt, Nk / kBkPair);
+  int t_act = nkt;
+  if constexpr (CAUSAL) {
+    t_full = min(t_full, max(0, floor_div(qw0 + qoff - (kBkPair - 1), kBkPair) + 1));
+    t_act = min(nkt, (qw0 + qoff + 31) / kBkPair + 1);
+  }
+  t_full = __builtin_amdgcn_readfirstlane(t_full);
+  t_act = __builtin_amdgcn_readfirstlane(t_act);
+  stage(0);
+  if (role == 0) {
+    bf16x8 qf[KS], gf[KS];
+    {
+      const int64_t qr = base + (int64_t)qc * rs;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qr + (2 * ks + hh) * 8);
+        gf[ks] = *reinterpret_cast<const bf16x8*>(a.dout + qr + (2 * ks + hh) * 8);
       }
     }
-  };
-  int t_full = min(nkt, Nk / kBkSplit);
-  if constexpr (CAUSAL) t_full = min(t_full, max(0, floor_div(qw0 + qoff - (kBkSplit - 1), kBkSplit) + 1));
-  t_full = __builtin_amdgcn_readfirstlane(t_full);
-  stage_rows(a.k, 0, kbuf);
-  stage_rows(a.v, 0, vbuf);
-  int t = 0;
-  for (; t < t_full; ++t) step(t, std::true_type{});
-  for (; t < nkt; ++t) step(t, std::false_type{});
-
-  if (myq < N) store_row_frags<DH>(a.dq + base + (int64_t)myq * rs + dh * DH, dq, hh, a.scale);
+    const float nl2 = a.ws[a.bhn + (int64_t)bh * N + qc];
+    const float ndval = a.ws[(int64_t)bh * N + qc];   // -D of this lane's query
+    // S^T and dP^T - D (lane = query, register r = key 8(r/4) + 4hh + r%4 of
+    // the step), then P^T, dS^T and its publication for step t.
+    auto score_step = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const char* kt = slot_of(t);
+      const int k0 = t * kBkPair;
+      f32x16 sacc = (f32x16){}, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pacc[r] = ndval;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sacc = mfma32x32x16(lds_read_b128(kt, rfb ^ (ks << 5)), qf[ks], sacc);
+        pacc = mfma32x32x16(lds_read_b128(kt + TILE, rfb ^ (ks << 5)), gf[ks], pacc);
+      }
+      bf16x8* const dso = dsbuf(t);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * u + e;
+          float pv = fast_exp2(__builtin_fmaf(sacc[r], c, nl2));
+          if constexpr (MASK) {
+            const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool hide = key >= Nk || (CAUSAL && key > myq + qoff);
+            pv = hide ? 0.f : pv;
+          }
+          ds[e] = pv * pacc[r];
+        }
+        dso[64 * u + lane] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+      }
+    };
+    int t = 0;
+    for (; t < t_full; ++t) { sync_stage(t); score_step(t, std::false_type{}); }
+    for (; t < t_act; ++t) { sync_stage(t); score_step(t, std::true_type{}); }
+    for (; t < nkt; ++t) sync_stage(t);
+    block_sync();   // the dQ wave reads the last step's dS after this barrier
+  } else {
+    f32x16 dq[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) dq[t] = (f32x16){};
+    // dQ^T += K^T dS^T (rows d, columns queries) with step t's dS^T.
+    auto dq_step = [&](int t) __attribute__((always_inline)) {
+      const char* kt = slot_of(t);
+      const bf16x8* const dsi = dsbuf(t);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 db = dsi[64 * u + lane];
+#pragma unroll
+        for (int t2 = 0; t2 < DT; ++t2) dq[t2] = mfma32x32x16(tr_frag<D>(kt, tfb, t2, 0, u), db, dq[t2]);
+      }
+    };
+    // Step t's barrier publishes the dS of step t - 1; K of step t - 1 stays
+    // in its slot until the barrier of step t + 1.
+    int t = 0;
+    for (; t < nkt; ++t) {
+      sync_stage(t);
+      if (t >= 1 && t <= t_act) dq_step(t - 1);
+    }
+    block_sync();
+    if (t_act == nkt && nkt > 0) dq_step(nkt - 1);
+    if (myq < N) store_row_frags<D>(a.dq + base + (int64_t)myq * rs, dq, hh, a.scale);
+  }
 }
 
 // ------------------------------------------------------------------ kernels
@@ -1004,8 +1225,8 @@ __device__ __forceinline__ void dq_tile_split(const BwdArgs& a, int bh, int qtil
 // dQ tile, which the compiler would give about 280, spills 57 dwords, and
 // is still 1.44x faster than at one wave per SIMD).  d = 256: 1 (the dK and
 // dV accumulators of a wave alone take 256 registers; a few more spill
-// without the mask); these one-wave tiles serve d = 256 with dropout and the
-// fused grid without the mask, the column-split kernels the rest.
+// without the mask); these one-wave tiles serve d = 256 with dropout, the
+// eight-wave pair kernels the rest.
 template <int D, bool CAUSAL, bool DROP>
 constexpr int bwd_min_waves() {
   return D == 64 ? (CAUSAL || !DROP ? 3 : 2) : D == 128 ? 2 : 1;
@@ -1019,20 +1240,21 @@ __global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL, DROP>())) void bwd_d
   dkdv_tile<D, CAUSAL, DROP>(a, bh, kt, smem);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kSplitWaves * 64, 2) void bwd_dkdv_split_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[dkdv_split_lds_bytes<D>()];
+template <int D, bool CAUSAL, bool KV_SPLIT>
+__global__ __launch_bounds__(kPairWaves * 64, 2) void bwd_dkdv_pair_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[KV_SPLIT ? dkdv_split_lds_bytes<D>() : dkdv_pair_lds_bytes<D>()];
   int bh, kt;
   tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, false, bh, kt);
-  dkdv_tile_split<D, CAUSAL>(a, bh, kt, smem);
+  if constexpr (KV_SPLIT) dkdv_tile_split<D, CAUSAL>(a, bh, kt, smem);
+  else dkdv_tile_pair<D, CAUSAL>(a, bh, kt, smem);
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kSplitWaves * 64, 2) void bwd_dq_split_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[dq_split_lds_bytes<D>()];
+__global__ __launch_bounds__(kPairWaves * 64, 2) void bwd_dq_pair_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[dq_pair_lds_bytes<D>()];
   int bh, qt;
   tile_of(blockIdx.x, a.ntiles, a.BH, CAUSAL, true, bh, qt);
-  dq_tile_split<D, CAUSAL>(a, bh, qt, smem);
+  dq_tile_pair<D, CAUSAL>(a, bh, qt, smem);
 }
 
 // Single-pass backward: the dK/dV tiles also add their share of dQ with fp32
@@ -1120,17 +1342,22 @@ __device__ __forceinline__ void fused_task(int id, int nt, int bhcount, bool cau
   bh = group * hpg + pos;
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kSplitWaves * 64, 2) void bwd_fused_split_kernel(BwdArgs a) {
-  static_assert(CAUSAL, "launched under the causal mask only");
-  constexpr int LDS = dkdv_split_lds_bytes<D>() > dq_split_lds_bytes<D>() ? dkdv_split_lds_bytes<D>()
-                                                                          : dq_split_lds_bytes<D>();
+// d = 256: both passes in one grid of eight-wave workgroups; KV_SPLIT takes
+// the column-split dK/dV tiles, else the role pairs.
+template <int D, bool CAUSAL, bool KV_SPLIT>
+__global__ __launch_bounds__(kPairWaves * 64, 2) void bwd_fused_pair_kernel(BwdArgs a) {
+  constexpr int KV = KV_SPLIT ? dkdv_split_lds_bytes<D>() : dkdv_pair_lds_bytes<D>();
+  constexpr int LDS = KV > dq_pair_lds_bytes<D>() ? KV : dq_pair_lds_bytes<D>();
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   bool is_kv;
   int bh, tile;
   fused_task(blockIdx.x, a.ntiles, a.BH, CAUSAL, is_kv, bh, tile);
-  if (is_kv) dkdv_tile_split<D, CAUSAL>(a, bh, tile, smem);
-  else dq_tile_split<D, CAUSAL>(a, bh, tile, smem);
+  if (is_kv) {
+    if constexpr (KV_SPLIT) dkdv_tile_split<D, CAUSAL>(a, bh, tile, smem);
+    else dkdv_tile_pair<D, CAUSAL>(a, bh, tile, smem);
+  } else {
+    dq_tile_pair<D, CAUSAL>(a, bh, tile, smem);
+  }
 }
 
 template <int D, bool CAUSAL, bool DROP>
@@ -1158,8 +1385,8 @@ hipError_t run_dkdv(BwdArgs a, int BH, bool causal, hipStream_t st) {
   a.ntiles = (a.Nk + kKeysPerWg - 1) / kKeysPerWg;
   const dim3 grid(a.ntiles * BH);
   if constexpr (D == 256 && !DROP) {
-    if (causal) hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, true>), grid, dim3(kSplitWaves * 64), 0, st, a);
-    else hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, false>), grid, dim3(kSplitWaves * 64), 0, st, a);
+    if (causal) hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, true, true>), grid, dim3(kPairWaves * 64), 0, st, a);
+    else hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, false, false>), grid, dim3(kPairWaves * 64), 0, st, a);
     return hipGetLastError();
   }
   if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, DROP>), grid, dim3(256), 0, st, a);
@@ -1172,8 +1399,8 @@ hipError_t run_dq(BwdArgs a, int BH, bool causal, hipStream_t st) {
   a.ntiles = (a.N + kQPerWg - 1) / kQPerWg;
   const dim3 grid(a.ntiles * BH);
   if constexpr (D == 256 && !DROP) {
-    if (causal) hipLaunchKernelGGL((bwd_dq_split_kernel<D, true>), grid, dim3(kSplitWaves * 64), 0, st, a);
-    else hipLaunchKernelGGL((bwd_dq_split_kernel<D, false>), grid, dim3(kSplitWaves * 64), 0, st, a);
+    if (causal) hipLaunchKernelGGL((bwd_dq_pair_kernel<D, true>), grid, dim3(kPairWaves * 64), 0, st, a);
+    else hipLaunchKernelGGL((bwd_dq_pair_kernel<D, false>), grid, dim3(kPairWaves * 64), 0, st, a);
     return hipGetLastError();
   }
   if (causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, DROP>), grid, dim3(256), 0, st, a);
@@ -1186,14 +1413,13 @@ hipError_t run_fused(BwdArgs a, int BH, bool causal, hipStream_t st) {
   // Square attention only (N == Nk): key tiles == query tiles, both 128 rows.
   a.ntiles = (a.N + kKeysPerWg - 1) / kKeysPerWg;
   const dim3 grid(2 * a.ntiles * BH);
-  // d = 256 under the mask: the column-split tiles (1.26x on [2, 4096, 16,
-  // 256]).  Without the mask the split grid spills and was 2% slower than the
-  // one-wave tiles, which it keeps.
+  // d = 256: the eight-wave pair tiles; dK/dV by column halves under the
+  // mask (1.092 against 1.136 ms on [2, 4096, 16, 256] with the role pairs),
+  // by role pairs without it (1.908 against 2.022 ms).
   if constexpr (D == 256 && !DROP) {
-    if (causal) {
-      hipLaunchKernelGGL((bwd_fused_split_kernel<D, true>), grid, dim3(kSplitWaves * 64), 0, st, a);
-      return hipGetLastError();
-    }
+    if (causal) hipLaunchKernelGGL((bwd_fused_pair_kernel<D, true, true>), grid, dim3(kPairWaves * 64), 0, st, a);
+    else hipLaunchKernelGGL((bwd_fused_pair_kernel<D, false, false>), grid, dim3(kPairWaves * 64), 0, st, a);
+    return hipGetLastError();
   }
   if (causal) hipLaunchKernelGGL((bwd_fused_kernel<D, true, DROP>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((bwd_fused_kernel<D, false, DROP>), grid, dim3(256), 0, st, a);

@@ -98,8 +98,9 @@ def test_cross_forward_and_backward(B, Nq, Nk, H, causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_separate_passes(shape, causal):
     """fa_backward_preprocess, fa_backward_dkdv and fa_backward_dq launched
-    apart (at this head size the column-split tiles: wave pairs that share
-    rows and split the columns) against the oracle.  Under the mask
+    apart (at this head size eight-wave workgroups whose wave pairs share
+    rows: dQ by a score wave and a dQ wave; dK/dV by role pairs without the
+    mask and by column-split pairs under it) against the oracle.
     fa_backward runs the same tiles as one grid and gives the same bits."""
     require_gpu()
     fa_ = fa
@@ -121,9 +122,8 @@ def test_separate_passes(shape, causal):
             dq_r, dk_r, dv_r, _ = ora.backward(qh, kh, vh, doh, scale, causal)
             for name, got, ref in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
                 check(to64(got[b, :, h]), ref, "bf16", f"d256 separate {name} b={b} h={h}")
-    if causal:
-        fused = fa_.backward(q, k, v, o, do, lse, scale=scale, causal=True)
-        torch.cuda.synchronize()
-        for name, a, b_ in zip(("dQ", "dK", "dV"), (dq, dk, dv), fused):
-            assert torch.equal(a, b_), f"{name}: separate passes and fa_backward differ"
+    fused = fa_.backward(q, k, v, o, do, lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    for name, a, b_ in zip(("dQ", "dK", "dV"), (dq, dk, dv), fused):
+        assert torch.equal(a, b_), f"{name}: separate passes and fa_backward differ"
     say("  ok")

@@ -96,7 +96,7 @@ def test_forward_backward(shape, causal):
         a, b = _both(noalloc)
         _same(a, b, ("dQ noalloc", "dK noalloc", "dV noalloc"))
     if d == 256:
-        # the separate passes (column-split tiles at this head size)
+        # the separate passes (eight-wave pair tiles at this head size)
         def separate():
             ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device="cuda")
             dq, dk, dv = (torch.empty_like(q) for _ in range(3))
