@@ -30,7 +30,8 @@
 //    for every copy in flight before the builtin form of that read.
 //  * exp is exp2 with scale*log2(e) folded into one FMA.  The reference max is
 //    only moved when a row's max grows by more than 2^8 (kRescaleLog2), or,
-//    without a mask, when a row's share of the sum exceeds 2^16: any
+//    in the unmasked steps of most forms, when a row's share of the sum
+//    exceeds 2^16 (the row max is then not computed at all): any
 //    finite reference gives the same O and LSE (the final divide uses the same
 //    reference), so this keeps exactness while the O rescale becomes rare.
 //  * Causal: tiles above the diagonal are never visited; waves whose 32 rows
@@ -82,6 +83,17 @@ constexpr int fwd_wg_waves() { return fwd_mode<D, CAUSAL, DROP>() == 3 || (D == 
 template <int D, bool DROP, int W = 4>
 constexpr int fwd_waves() { return D == 64 ? (DROP ? 3 : 4) : D == 128 ? 2 : (W == 8 ? 2 : 1); }
 constexpr int kWide256Grid = 512;
+// How unmasked steps after the first keep the reference max: lazily (P
+// against the current reference first, the row max only when a row's share
+// of the sum exceeds 2^16, then the step redone) or eagerly (the row max
+// first, the reference moved when it grows by more than 2^8, one pass of
+// exponentials).  The lazy form saves the max at D = 64 and 128 and at
+// D = 256 without the mask; under the mask at D = 256 (12-15% faster) and
+// with dropout (2-6%) the redo path's second copy of the exponentials (and
+// of the generator calls) costs more registers than the max (measured on
+// MI355X).
+template <int D, bool CAUSAL, bool DROP>
+constexpr bool fwd_eager_max() { return (D == 256 && CAUSAL) || DROP; }
 
 // Buffer index carried by a step's buffer tag: the constant of a
 // compile-time tag, 0 for a run-time one (whose offset is in the pointer).
@@ -264,9 +276,11 @@ __global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_b
   // Softmax update for one step: P (bf16 operands) of the step's scores.
   //  MASK steps (diagonal or ragged end) hide keys and move the reference to
   //  the exact running max when it grows by more than 2^8.
-  //  Other steps exponentiate against the current reference straight away and
-  //  only look at the row max (and redo the step) if some row's share of the
-  //  sum exceeds 2^16, which bounds every probability by 2^16.
+  //  Other steps, in the lazy form, exponentiate against the current
+  //  reference straight away and only look at the row max (and redo the
+  //  step) if some row's share of the sum exceeds 2^16, which bounds every
+  //  probability by 2^16; in the eager form (fwd_eager_max) they look at the
+  //  row max first, as MASK steps do.
   //  The first step of a wave, when no key of it is hidden (mask_tag of
   //  value 2), sets the reference to the row max before exponentiating: the
   //  reference is -inf before it, so exponentiating first would always redo
@@ -301,6 +315,14 @@ __global__ __launch_bounds__((64 * WGW), (fwd_waves<D, DROP, WGW>())) void fwd_b
       const float mcand = (mx == -INFINITY) ? -INFINITY : mx * c;
       if (__any(fmaxf(m_ref, mcand) > m_ref + kRescaleLog2)) move_reference(s);
       lsum = exp_tile(std::true_type{}, s, pb, k0);
+    } else if constexpr (fwd_eager_max<D, CAUSAL, DROP>()) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+      if (__any(max_halves(mx) * c > m_ref + kRescaleLog2)) move_reference(s);
+      lsum = exp_tile(std::false_type{}, s, pb, k0);
     } else {
       lsum = exp_tile(std::false_type{}, s, pb, k0);
       if (__any(!(lsum <= kSumLimit))) {
