@@ -69,6 +69,12 @@ struct BwdArgs {
 // Rows go in [B, H, N] order (the order of the outputs), so a workgroup's
 // writes of -D and -LSE log2 e are contiguous and each row read is a whole
 // D*2-byte run (in [B, N, H] order each output word was a line of its own).
+// A workgroup takes 64 rows: each lane group of CH lanes handles RPT = CH/4
+// of them and issues all their loads before the first reduction (at D = 128
+// and 256 one row per lane group left the loads too few in flight: 23 against
+// 38 us and 30 against 38 us on MI355X).
+constexpr int kPreRowsPerWg = 64;
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ o,
                                                       const __bf16* __restrict__ dout,
@@ -76,24 +82,38 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
                                                       float* __restrict__ ws, int H, int N,
                                                       int64_t rows, int64_t bhn) {
   constexpr int CH = D / 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t idx = gid / CH;            // output index (b H + h) N + n
-  const int ch = (int)(gid % CH);
-  float acc = 0.f;
-  if (idx < rows) {
-    const int64_t n = idx % N, bh = idx / N;
-    const int64_t h = bh % H, b = bh / H;
-    const int64_t r = (b * N + n) * H + h;  // row of the [B, N, H, d] tensors
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + r * D + ch * 8);
-    const bf16x8 y = *reinterpret_cast<const bf16x8*>(dout + r * D + ch * 8);
+  constexpr int GROUPS = 256 / CH;                 // lane groups per workgroup
+  constexpr int RPT = kPreRowsPerWg / GROUPS;      // rows per lane group
+  static_assert(RPT * GROUPS == kPreRowsPerWg && RPT >= 1, "rows per workgroup");
+  const int grp = threadIdx.x / CH;
+  const int ch = threadIdx.x % CH;
+  const int64_t row0 = (int64_t)blockIdx.x * kPreRowsPerWg + grp;   // rows row0 + GROUPS i
+  bf16x8 x[RPT], y[RPT];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
+  for (int i = 0; i < RPT; ++i) {
+    const int64_t idx = row0 + GROUPS * i;   // output index (b H + h) N + n
+    if (idx < rows) {
+      const int64_t n = idx % N, bh = idx / N;
+      const int64_t h = bh % H, b = bh / H;
+      const int64_t r = (b * N + n) * H + h;  // row of the [B, N, H, d] tensors
+      x[i] = *reinterpret_cast<const bf16x8*>(o + r * D + ch * 8);
+      y[i] = *reinterpret_cast<const bf16x8*>(dout + r * D + ch * 8);
+    }
   }
 #pragma unroll
-  for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CH);
-  if (idx < rows && ch == 0) {
-    ws[idx] = -acc;
-    ws[bhn + idx] = -lse[idx] * kLog2e;
+  for (int i = 0; i < RPT; ++i) {
+    const int64_t idx = row0 + GROUPS * i;
+    float acc = 0.f;
+    if (idx < rows) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[i][e], (float)y[i][e], acc);
+    }
+#pragma unroll
+    for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CH);
+    if (idx < rows && ch == 0) {
+      ws[idx] = -acc;
+      ws[bhn + idx] = -lse[idx] * kLog2e;
+    }
   }
 }
 
@@ -1374,8 +1394,7 @@ __global__ __launch_bounds__(256, (bwd_min_waves<D, CAUSAL, DROP>())) void bwd_f
 template <int D>
 hipError_t run_pre(const BwdArgs& a, int B, hipStream_t st) {
   const int64_t rows = (int64_t)B * a.N * a.H;
-  const int64_t threads = rows * (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + kPreRowsPerWg - 1) / kPreRowsPerWg)), dim3(256), 0, st,
                      a.o, a.dout, a.lse, a.ws, a.H, a.N, rows, a.bhn);
   return hipGetLastError();
 }
