@@ -23,9 +23,10 @@ workloads ([4, 4096, 16, 128] and [1, 32768, 32, 128] with Q, K doubled);
 
 runs only a plain device copy of 256 MiB (for scaling hardware byte counters).
 
-    python bench.py --kernel-case {c5,c3_causal,c3_noncausal,c4,c2} [--steps K]
+    python bench.py --kernel-case {c5,c3_causal,c3_noncausal,c4,c2,h256_causal} [--steps K]
 
-runs only that workload's launches (c5: the forward + backward step; the
+runs only that workload's launches (c5: the forward + backward step;
+h256_causal: fa_forward and fa_backward at [2, 4096, 16, 256] causal; the
 others: the forward), for profiling one kernel under rocprofv3.
 
 Besides the back-to-back timing that gives `value`, the line carries per-kernel
@@ -470,6 +471,12 @@ def kernel_case(fa, torch, synth, name, steps):
         "c4": (1, 32768, 32, 128, True, 2.0, 4),
         "c2": (2, 512, 8, 64, True, 1.0, 2),
     }
+    if name == "h256_causal":
+        # fa_forward then fa_backward (preprocess + the fused grid) on
+        # [2, 4096, 16, 256] causal, as in the line's head256 block.
+        r = time_fwd_bwd(fa, torch, 2, 4096, 16, 256, True, steps)
+        print(json.dumps({"kernel_case": name, **r}), flush=True)
+        return
     B, N, H, d, causal, mult, seed = cases[name]
     r = time_forward_only(fa, torch, B, N, H, d, synth.f32(d ** -0.5) if d != 64 else 0.125, mult, seed, steps,
                           causal=causal)
@@ -484,7 +491,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--kernel-case", choices=["c5", "c3_causal", "c3_noncausal", "c4", "c2"])
+    ap.add_argument("--kernel-case", choices=["c5", "c3_causal", "c3_noncausal", "c4", "c2", "h256_causal"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (heads would shard "
