@@ -1085,13 +1085,14 @@ __device__ __forceinline__ void dq_tile(const BwdArgs& a, int bh, int qtile, cha
 // takes it, which it hands to its partner through LDS.  The dQ wave (w + 4)
 // holds the dQ accumulators and, one step behind, adds dQ^T += K^T dS^T.
 // The products and elementwise operations are the one-wave tile's in the
-// same order (bitwise the same dQ).  K and V rotate through three 32-key
-// slot pairs: the dQ wave reads K of the step before the score wave's.
+// same order (bitwise the same dQ).  K and V rotate through four 32-key
+// slot pairs, copied two steps ahead: the dQ wave reads K of the step before
+// the score wave's (two steps ahead instead of one: 2-3% faster).
 constexpr int kBkPair = 32;
 constexpr int kDsBytes = 4 * 64 * 32;   // dS^T of one step: 4 pairs x 64 lanes x 16 bf16
 
 template <int D>
-constexpr int dq_pair_lds_bytes() { return 3 * 2 * kBkPair * D * 2 + 2 * kDsBytes; }
+constexpr int dq_pair_lds_bytes() { return 4 * 2 * kBkPair * D * 2 + 2 * kDsBytes; }
 
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_tile_pair(const BwdArgs& a, int bh, int qtile, char* smem) {
@@ -1099,7 +1100,7 @@ __device__ __forceinline__ void dq_tile_pair(const BwdArgs& a, int bh, int qtile
   constexpr int TILE = kBkPair * RB;       // one K or V tile
   constexpr int CPW = TILE / 1024 / kPairWaves;
   static_assert(CPW * kPairWaves * 1024 == TILE, "the copies cover the tile");
-  static_assert(6 * TILE + 2 * kDsBytes == dq_pair_lds_bytes<D>(), "LDS layout");
+  static_assert(8 * TILE + 2 * kDsBytes == dq_pair_lds_bytes<D>(), "LDS layout");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -1119,11 +1120,11 @@ __device__ __forceinline__ void dq_tile_pair(const BwdArgs& a, int bh, int qtile
   const int kend = CAUSAL ? min(Nk, q0 + qoff + kQPerWg) : Nk;
   const int nkt = (kend + kBkPair - 1) / kBkPair;
 
-  auto slot_of = [&](int t) { return smem + (t % 3) * (2 * TILE); };   // K, then V
+  auto slot_of = [&](int t) { return smem + (t & 3) * (2 * TILE); };   // K, then V
   // dS^T of step t: 16-byte unit 64 u + lane of this pair's area holds the
   // bf16 operand of half u (registers 8 u .. 8 u + 7) of the lane.
   auto dsbuf = [&](int t) {
-    return reinterpret_cast<bf16x8*>(smem + 6 * TILE + (t & 1) * kDsBytes) + qg * 2 * 64;
+    return reinterpret_cast<bf16x8*>(smem + 8 * TILE + (t & 1) * kDsBytes) + qg * 2 * 64;
   };
   uint32_t voff[CPW];
   stage_offsets<D, CPW, kPairWaves>(voff, wave, lane, rs);
@@ -1139,10 +1140,15 @@ __device__ __forceinline__ void dq_tile_pair(const BwdArgs& a, int bh, int qtile
       buffer_to_lds16(rv, voff[i], slot + TILE + (wu + kPairWaves * i) * 1024);
     }
   };
+  // Start of step t for every wave: this wave's copies of tile t complete
+  // (those of tile t + 1, the only ones issued after them, may be in flight),
+  // then the barrier publishes everyone's, and tile t + 2 goes into the slot
+  // of tile t - 2.
   auto sync_stage = [&](int t) {
-    wait_vmem();
+    if (t + 1 < nkt) wait_vmem_n<2 * CPW>();
+    else wait_vmem();
     block_sync();
-    if (t + 1 < nkt) stage(t + 1);
+    if (t + 2 < nkt) stage(t + 2);
   };
   const uint32_t rfb = row_frag_base<D>(lane);
   const uint32_t tfb = tr_frag_base<D>(lane);
@@ -1160,6 +1166,7 @@ __device__ __forceinline__ void dq_tile_pair(const BwdArgs& a, int bh, int qtile
   t_full = __builtin_amdgcn_readfirstlane(t_full);
   t_act = __builtin_amdgcn_readfirstlane(t_act);
   stage(0);
+  if (nkt > 1) stage(1);
   if (role == 0) {
     bf16x8 qf[KS], gf[KS];
     {
