@@ -32,9 +32,11 @@
 // score wave and a dQ wave, dK/dV by a P wave and a dS wave without the mask
 // and by column halves under it (each the faster form there on MI355X).
 // Both passes stage their streamed tiles with buffer -> LDS copies into two
-// LDS slots.  At head size 64 these plain loops at three waves per SIMD
-// measured faster than software-pipelined forms (the score products of the
-// next tile issued ahead of the exp / dS work of the current one) at two.
+// LDS slots (three or four in the d = 256 role-pair tiles, whose lagging wave
+// still reads the previous tile).  At head size 64 these plain loops at three
+// waves per SIMD measured faster than software-pipelined forms (the score
+// products of the next tile issued ahead of the exp / dS work of the current
+// one) at two.
 #include <type_traits>
 
 #include "fa_common.hpp"
