@@ -127,3 +127,24 @@ def test_separate_passes(shape, causal):
     for name, a, b_ in zip(("dQ", "dK", "dV"), (dq, dk, dv), fused):
         assert torch.equal(a, b_), f"{name}: separate passes and fa_backward differ"
     say("  ok")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_repeats_bitwise(causal):
+    """The eight-wave pair tiles hand scores or probabilities from one wave to
+    its partner through LDS and copy tiles one or two steps ahead: four calls
+    of fa_backward on the same inputs give the same bits (a missing wait would
+    let a read see a slot's previous contents in some calls and not others)."""
+    require_gpu()
+    shape = (2, 1000, 4, D)
+    say(f"d256 backward repeats shape={shape} causal={causal}")
+    dev, _ = inputs(shape, "bf16", 6700, with_do=True)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o, lse = fa.forward(q, k, v, causal=causal)
+    first = fa.backward(q, k, v, o, do, lse, causal=causal)
+    for _ in range(3):
+        again = fa.backward(q, k, v, o, do, lse, causal=causal)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dQ", "dK", "dV"), first, again):
+            assert torch.equal(a, b), f"{name}: fa_backward gave different bits on a repeated call"
+    say("  ok")
