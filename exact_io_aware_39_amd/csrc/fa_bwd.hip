@@ -719,7 +719,7 @@ __device__ __forceinline__ void dkdv_tile_pair(const BwdArgs& a, int bh, int kt,
 // fp32, and both waves go on from the same sums (a + b and b + a are the
 // same fp32 value); each then updates its own columns of dV and dK.  The
 // launchers take this tile under the causal mask.
-constexpr int kSplitWaves = 8;
+constexpr int kSplitWaves = kPairWaves;   // launched by the same eight-wave kernels
 constexpr int kXchgBytes = kSplitWaves * 64 * 32 * 4;   // 32 floats per lane and wave
 
 template <int D>
