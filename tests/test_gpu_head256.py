@@ -148,3 +148,14 @@ def test_backward_repeats_bitwise(causal):
         for name, a, b in zip(("dQ", "dK", "dV"), first, again):
             assert torch.equal(a, b), f"{name}: fa_backward gave different bits on a repeated call"
     say("  ok")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_bench_shape_sampled_heads(causal):
+    """The bench's d = 256 workload, [2, 4096, 16, 256], in the launch
+    configuration it times (fa_forward + fa_backward: eight-wave pair tiles
+    over 2048 workgroups); two heads checked element by element against the
+    oracle (each an fp64 4096 x 4096 problem)."""
+    require_gpu()
+    heads = [(0, 0), (1, 15)] if causal else [(1, 7)]
+    run_backward((2, 4096, 16, D), "bf16", 6800, causal, D ** -0.5, heads=heads, tag="d256 bench shape")
