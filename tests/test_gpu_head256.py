@@ -159,3 +159,12 @@ def test_backward_bench_shape_sampled_heads(causal):
     require_gpu()
     heads = [(0, 0), (1, 15)] if causal else [(1, 7)]
     run_backward((2, 4096, 16, D), "bf16", 6800, causal, D ** -0.5, heads=heads, tag="d256 bench shape")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_bench_shape_sampled_heads(causal):
+    """The bench's d = 256 forward, [2, 4096, 16, 256], in the launch
+    configuration it times (the 8-wave form over 512 workgroups; under the
+    mask with the eager reference max), two heads against the oracle."""
+    require_gpu()
+    run_forward((2, 4096, 16, D), "bf16", 6900, causal, D ** -0.5, heads=[(0, 3), (1, 12)], tag="d256 bench shape")
