@@ -69,6 +69,23 @@ def test_decode_long_cache_all_heads():
     _check_heads(o, lse, f64, scale, True, [(b, h) for b in range(B) for h in range(H)], "long cache")
 
 
+@pytest.mark.parametrize("Nq", [1, 4])
+def test_decode_bench_shape_sampled_heads(Nq):
+    """The bench's decode workload, [B, Nq, Nk, H, d] = [8, Nq, 32768, 32,
+    128] causal, in the launch configuration it times (the library's chunk
+    count: 4 chunks per head, 1024 workgroups); eight heads spread over the
+    batch against the oracle."""
+    require_gpu()
+    B, Nk, H, d = 8, 32768, 32, 128
+    say("decode bench shape", B, Nq, Nk, H, d)
+    dev, f64 = _inputs(B, Nq, Nk, H, d, seed=11)
+    scale = synth.f32(d ** -0.5)
+    o, lse = fa.decode(dev["q"], dev["k"], dev["v"], scale=scale, causal=True)
+    torch.cuda.synchronize()
+    heads = [(b, (5 * b + 3) % H) for b in range(B)]
+    _check_heads(o, lse, f64, scale, True, heads, "bench shape")
+
+
 def test_decode_sharp_softmax():
     """Q and K doubled (logit standard deviation about 4): a few keys dominate."""
     require_gpu()
